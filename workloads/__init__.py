@@ -1,0 +1,221 @@
+"""Seeded synthetic inputs for the sparse-MLA writer and attention.
+
+This module only draws random numbers and lays them out.  It holds none of the
+method's arithmetic (no quantisation, no attention), so that the CPU oracle and
+the HIP path can both be fed from it without sharing any of the computation.
+
+Shapes follow the workloads the source pages describe:
+
+* sglang PR 47013 (zero-RoPE writer skips slot 0), Speed Tests: writer calls of
+  1,024 and 8,192 bf16 rows of 512 values, a quarter of them padding rows
+  aimed at slot 0; decode at 16 heads, d_v 512, top-k 2048, 1-256 tokens.
+* sglang PR 39288 (SM120 page-split scratch), Root cause and kernel-harness
+  table: 64-token pages, H=16, -1 padding, slot 0 holding 0xFF, random or zero
+  bytes, prefill T=65 / decode T=64 boundary.
+* vLLM PR 55277 (NoPE sparse MLA on SM120), Purpose (1) and (2): the 656-byte
+  fp8_ds_mla row also for NoPE models, and a top-k buffer of width 2176
+  (index_topk 2048 plus a 128-wide tail).
+
+All arrays are numpy; bf16 values are carried as their uint16 bit patterns.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+PAGE = 64               # tokens per page (sglang PR 39288, Root cause (2))
+LATENT = 512            # latent width (vLLM PR 55277, Purpose (1))
+ROPE = 64               # RoPE width when present
+ROW_BYTES = 656         # packed fp8_ds_mla row
+
+BF16_QNAN = np.uint16(0x7FC0)
+
+
+def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (round to nearest, ties to even); return bits.
+
+    Inputs are finite (the generators only draw normals)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def f32_from_bf16_bits(b: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns to float32 (exact)."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def normal_bf16(rng: np.random.Generator, shape) -> np.ndarray:
+    """bf16 bits of N(0,1) samples drawn in float32."""
+    return bf16_bits_from_f32(rng.standard_normal(shape, dtype=np.float32))
+
+
+# --------------------------------------------------------------------------
+# top-k index builders
+# --------------------------------------------------------------------------
+
+def decode_topk(rng: np.random.Generator, T: int, width: int, num_slots: int,
+                ctx_lo: int, ctx_hi: int, index_topk: int = 2048) -> np.ndarray:
+    """Per-token top-k slot lists for decode.
+
+    Each token owns a context of L ~ U{ctx_lo..ctx_hi} tokens laid out on
+    ceil(L/64) distinct random pages (page 0 is reserved, as sglang reserves
+    full-pool page 0).  min(L, index_topk) distinct positions of the context are
+    drawn without replacement in random order and mapped to their slots; the
+    rest of the row, up to `width`, is -1.
+    """
+    n_pages = num_slots // PAGE
+    out = np.full((T, width), -1, dtype=np.int32)
+    for t in range(T):
+        L = int(rng.integers(ctx_lo, ctx_hi + 1))
+        pages = rng.choice(n_pages - 1, size=(L + PAGE - 1) // PAGE, replace=False) + 1
+        n = min(L, index_topk, width)
+        pos = rng.choice(L, size=n, replace=False)
+        out[t, :n] = (pages[pos // PAGE] * PAGE + pos % PAGE).astype(np.int32)
+    return out
+
+
+def prefill_topk(rng: np.random.Generator, T: int, width: int, num_slots: int):
+    """Top-k lists of one causal sequence of T tokens.
+
+    The sequence sits on ceil(T/64) distinct random pages (page 0 excluded).
+    Row t lists the slots of tokens 0..t (all of them while t < width, else a
+    random subset of `width`), shuffled, then -1.  Returns (idx, seq_slots)."""
+    n_pages = num_slots // PAGE
+    pages = rng.choice(n_pages - 1, size=(T + PAGE - 1) // PAGE, replace=False) + 1
+    seq_slots = (pages[np.arange(T) // PAGE] * PAGE + np.arange(T) % PAGE).astype(np.int32)
+    out = np.full((T, width), -1, dtype=np.int32)
+    for t in range(T):
+        n = min(t + 1, width)
+        sel = rng.choice(t + 1, size=n, replace=False)
+        out[t, :n] = seq_slots[sel]
+    return out, seq_slots
+
+
+def disjoint_topk(rng: np.random.Generator, T: int, width: int, num_slots: int) -> np.ndarray:
+    """T rows of `width` slots, pairwise disjoint across the whole batch (slot 0 excluded)."""
+    assert T * width <= num_slots - 1
+    perm = rng.permutation(num_slots - 1)[: T * width] + 1
+    return perm.reshape(T, width).astype(np.int32)
+
+
+# --------------------------------------------------------------------------
+# whole workloads
+# --------------------------------------------------------------------------
+
+def cache_rows(rng: np.random.Generator, num_slots: int, rope_dim: int):
+    """bf16 latent and RoPE rows for every slot 1..num_slots-1 (row i -> slot i+1)."""
+    n = num_slots - 1
+    latent = normal_bf16(rng, (n, LATENT))
+    rope = normal_bf16(rng, (n, rope_dim)) if rope_dim else None
+    slots = np.arange(1, num_slots, dtype=np.int64)
+    return latent, rope, slots
+
+
+def slot0_bytes(rng: np.random.Generator, poison: str) -> np.ndarray:
+    """656 bytes for the reserved slot: 'ff', '7f', 'zero' or 'random'."""
+    if poison == "ff":
+        return np.full(ROW_BYTES, 0xFF, dtype=np.uint8)
+    if poison == "7f":
+        return np.full(ROW_BYTES, 0x7F, dtype=np.uint8)
+    if poison == "zero":
+        return np.zeros(ROW_BYTES, dtype=np.uint8)
+    if poison == "random":
+        return rng.integers(0, 256, size=ROW_BYTES, dtype=np.uint8)
+    raise ValueError(poison)
+
+
+def config_tiny(seed: int = 1) -> dict:
+    """Tiny decode: 4 pages x 64 = 256 slots, rope 64, slot 0 = 0xFF, T=2, H=4,
+    top-k 128 with 77 distinct random slots in 1..255 then 51 x -1."""
+    rng = np.random.default_rng(seed)
+    num_slots, rope_dim, T, H, W = 256, ROPE, 2, 4, 128
+    latent, rope, slots = cache_rows(rng, num_slots, rope_dim)
+    q = normal_bf16(rng, (T, H, LATENT + rope_dim))
+    n_pad = int(np.floor(0.4 * W))
+    idx = np.full((T, W), -1, dtype=np.int32)
+    for t in range(T):
+        idx[t, : W - n_pad] = rng.choice(np.arange(1, num_slots), size=W - n_pad, replace=False)
+    return dict(num_slots=num_slots, rope_dim=rope_dim, T=T, H=H, W=W,
+                latent=latent, rope=rope, slots=slots, q=q, idx=idx,
+                sm_scale=float(1.0 / np.sqrt(LATENT + rope_dim)),
+                slot0=slot0_bytes(rng, "ff"))
+
+
+def config_nope_decode(T: int, seed: int | None = None, num_slots: int = 131072,
+                       H: int = 16, ctx=(1024, 65536), W: int = 2176) -> dict:
+    """GLM-style NoPE decode: rope 0, H=16, 131,072-slot cache, contexts
+    U{1k..64k}, width 2176 (2048 + a 128-wide tail of -1), slot 0 = 0x7F."""
+    rng = np.random.default_rng(20 + T if seed is None else seed)
+    latent, rope, slots = cache_rows(rng, num_slots, 0)
+    q = normal_bf16(rng, (T, H, LATENT))
+    idx = decode_topk(rng, T, W, num_slots, ctx[0], ctx[1])
+    return dict(num_slots=num_slots, rope_dim=0, T=T, H=H, W=W,
+                latent=latent, rope=rope, slots=slots, q=q, idx=idx,
+                sm_scale=float(1.0 / np.sqrt(LATENT)), slot0=slot0_bytes(rng, "7f"))
+
+
+def config_rope_decode(T: int, seed: int | None = None, num_slots: int = 262144,
+                       H: int = 16, ctx=(2048, 131072), W: int = 2048) -> dict:
+    """DeepSeek-style RoPE decode: rope 64, H=16, top-k 2048, contexts
+    U{2k..128k}, 262,144-slot cache, slot 0 random bytes."""
+    rng = np.random.default_rng(30 + T if seed is None else seed)
+    latent, rope, slots = cache_rows(rng, num_slots, ROPE)
+    q = normal_bf16(rng, (T, H, LATENT + ROPE))
+    idx = decode_topk(rng, T, W, num_slots, ctx[0], ctx[1])
+    return dict(num_slots=num_slots, rope_dim=ROPE, T=T, H=H, W=W,
+                latent=latent, rope=rope, slots=slots, q=q, idx=idx,
+                sm_scale=float(1.0 / np.sqrt(LATENT + ROPE)), slot0=slot0_bytes(rng, "random"))
+
+
+def config_prefill(T: int, seed: int | None = None, num_slots: int = 131072,
+                   H: int = 16, W: int = 2048) -> dict:
+    """Sparse prefill: T query rows of one causal sequence; row t lists the
+    slots of tokens <= t then -1; rope 64; slot 0 random bytes."""
+    rng = np.random.default_rng(40 + T if seed is None else seed)
+    latent, rope, slots = cache_rows(rng, num_slots, ROPE)
+    q = normal_bf16(rng, (T, H, LATENT + ROPE))
+    idx, seq = prefill_topk(rng, T, W, num_slots)
+    return dict(num_slots=num_slots, rope_dim=ROPE, T=T, H=H, W=W,
+                latent=latent, rope=rope, slots=slots, q=q, idx=idx, seq_slots=seq,
+                sm_scale=float(1.0 / np.sqrt(LATENT + ROPE)), slot0=slot0_bytes(rng, "random"))
+
+
+def config_disjoint(T: int = 64, seed: int = 60, num_slots: int = 262144,
+                    H: int = 16, W: int = 2048) -> dict:
+    """RoPE decode whose top-k sets are pairwise disjoint across the batch, so
+    gathered bytes equal unique bytes (a control against cache reuse)."""
+    rng = np.random.default_rng(seed)
+    latent, rope, slots = cache_rows(rng, num_slots, ROPE)
+    q = normal_bf16(rng, (T, H, LATENT + ROPE))
+    idx = disjoint_topk(rng, T, W, num_slots)
+    return dict(num_slots=num_slots, rope_dim=ROPE, T=T, H=H, W=W,
+                latent=latent, rope=rope, slots=slots, q=q, idx=idx,
+                sm_scale=float(1.0 / np.sqrt(LATENT + ROPE)), slot0=slot0_bytes(rng, "random"))
+
+
+def config_writer(N: int = 8192, rope_dim: int = ROPE, seed: int = 50,
+                  num_slots: int = 131072, pad_frac: float = 0.25,
+                  shuffle: bool = False) -> dict:
+    """Standalone writer call: N rows, the trailing pad_frac of them padding rows
+    aimed at slot 0 whose inputs are bf16 NaN; the rest go to distinct random
+    slots >= 1.  The cache starts as 0xA5 except slot 0, which is zero."""
+    rng = np.random.default_rng(seed)
+    n_pad = int(round(N * pad_frac))
+    n_real = N - n_pad
+    latent = normal_bf16(rng, (N, LATENT))
+    rope = normal_bf16(rng, (N, rope_dim)) if rope_dim else None
+    slots = np.zeros(N, dtype=np.int64)
+    slots[:n_real] = rng.choice(num_slots - 1, size=n_real, replace=False) + 1
+    latent[n_real:] = BF16_QNAN
+    if rope is not None:
+        rope[n_real:] = BF16_QNAN
+    if shuffle:
+        perm = rng.permutation(N)
+        latent, slots = latent[perm], slots[perm]
+        if rope is not None:
+            rope = rope[perm]
+    cache = np.full((num_slots, ROW_BYTES), 0xA5, dtype=np.uint8)
+    cache[0] = 0
+    return dict(num_slots=num_slots, rope_dim=rope_dim, N=N, latent=latent,
+                rope=rope, slots=slots, cache=cache)
