@@ -1,0 +1,149 @@
+/*
+ * sparse_mla.h - C ABI of the MI355X (gfx950) sparse-MLA library.
+ *
+ * Two calls make up the hot path of DeepSeek/GLM-style sparse MLA decoding
+ * over a paged FP8 KV cache:
+ *
+ *   mla_kv_write     packs bf16 latent rows (+ optional RoPE) into 656-byte
+ *                    fp8_ds_mla cache rows, dropping writes aimed at the
+ *                    reserved padding slot 0;
+ *   sparse_mla_attn  attends every query row over its top-k list of cache
+ *                    slots, where a negative entry is padding.
+ *
+ * Common rules
+ *   - Every pointer argument is a DEVICE pointer owned by the caller; the
+ *     library allocates nothing and keeps no device state between calls.
+ *   - Calls are asynchronous on `stream` (0 = the null stream) and do not
+ *     synchronise.  They are reentrant; concurrent calls on different streams
+ *     must not write the same memory.
+ *   - Argument errors are detected on the host before any launch and return a
+ *     negative code; nothing is launched then.  smla_last_error() returns a
+ *     thread-local text for the last failing call on the calling thread.
+ *   - Device-side values (slots, indices) are not validated beyond the rules
+ *     stated per call; out-of-range ones are treated as "drop" / "padding".
+ *   - Offsets into the cache are 64-bit: slot * 656 does not wrap.
+ *   - Results are bitwise reproducible for the same inputs and sizes
+ *     (no floating-point atomics, fixed reduction order).
+ *
+ * Cache layout (vLLM PR 55277, "Support NoPE sparse MLA (GLM-5.3-Flash) on
+ * the FlashInfer SM120 backend", Purpose (1)): the cache is uint8
+ * [num_slots][656], slot = page * 64 + offset for 64-token pages
+ * (sglang PR 39288, Root cause (2)).  Row bytes:
+ *   [0, 512)    e4m3 codes (OCP "fn" encoding, NaN = 0x7F / 0xFF) of the
+ *               512-wide latent, four tiles of 128 values;
+ *   [512, 528)  the four tile scales, float32 little-endian, tile order;
+ *   [528, 656)  64 bf16 RoPE values, or zeros for NoPE rows (rope_dim 0).
+ */
+#ifndef SPARSE_MLA_H
+#define SPARSE_MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SMLA_OK            0
+#define SMLA_EINVAL       -1  /* bad argument (null pointer, size, alignment, rope_dim) */
+#define SMLA_EWORKSPACE   -2  /* workspace smaller than sparse_mla_attn_workspace_size() */
+#define SMLA_ELAUNCH      -3  /* the HIP runtime reported an error at launch */
+#define SMLA_EUNSUPPORTED -4  /* a size this build does not handle */
+
+#define SMLA_ROW_BYTES   656
+#define SMLA_LATENT      512
+#define SMLA_MAX_HEADS   128
+
+/*
+ * mla_kv_write - quantise and store MLA KV rows.
+ *
+ * Follows sglang PR 47013 ("zero-RoPE MLA KV writer skips reserved slot 0"),
+ * Summary and Modifications, and vLLM PR 55277, Purpose (1):
+ *   for each row i with 1 <= slot_mapping[i] < num_slots:
+ *     per 128-value tile t of the latent: amax_t = max |x|,
+ *       scale_t = fp32(amax_t / 448)  (IEEE float32 division);
+ *     code = e4m3(fp32(x / scale_t)), rounded to nearest even, saturating at
+ *       +-448; a tile with amax_t == 0 stores scale 0 and all-zero codes;
+ *     bytes [528,656) = the 64 RoPE values (rope_dim 64) or zeros (rope_dim 0).
+ *   Rows whose slot is 0 (the reserved padding slot), negative or
+ *   >= num_slots are dropped and their inputs are never read, so padding
+ *   rows may hold NaN.  No other cache byte is written.  Duplicate slots in
+ *   one call leave that slot holding one of the rows (unspecified which).
+ *   NaN inputs in kept rows are not sanitised.
+ *
+ * kv_c            bf16 [num_rows][>= 512], row stride kv_c_row_stride elements
+ *                 (multiple of 8), base 16-byte aligned.
+ * k_pe            bf16 [num_rows][>= 64] with stride k_pe_row_stride (multiple
+ *                 of 8, base 16-byte aligned) when rope_dim == 64; must be NULL
+ *                 when rope_dim == 0.
+ * rope_dim        64 or 0; anything else is SMLA_EINVAL.
+ * slot_mapping    int64 [num_rows].
+ * num_rows        >= 0 (0 launches nothing).
+ * kv_cache        uint8 [num_slots][656], 16-byte aligned; num_slots >= 1.
+ */
+int mla_kv_write(const void* kv_c, int64_t kv_c_row_stride,
+                 const void* k_pe, int64_t k_pe_row_stride,
+                 int rope_dim,
+                 const int64_t* slot_mapping, int64_t num_rows,
+                 void* kv_cache, int64_t num_slots,
+                 hipStream_t stream);
+
+/*
+ * sparse_mla_attn_workspace_size - bytes of device workspace that
+ * sparse_mla_attn needs for these sizes (0 when none is needed).  Pure host
+ * function; returns 0 for invalid sizes as well (sparse_mla_attn reports them).
+ */
+size_t sparse_mla_attn_workspace_size(int T, int H, int topk_capacity, int rope_dim);
+
+/*
+ * sparse_mla_attn - sparse MLA attention over the fp8_ds_mla cache.
+ *
+ * Follows sglang PR 47013, Motivation; sglang PR 39288 ("zero-initialise the
+ * 64-token page-split scratch so masked candidates never gather NaN from
+ * slot 0"), Root cause (1); and vLLM PR 55277, Purpose (1) and (2):
+ *   for query row t and head h, over the valid entries j of topk_idx[t][0..W)
+ *   (valid: 0 <= idx < num_slots; any other value is padding, anywhere in the
+ *   row; duplicates count once per entry):
+ *     K_j[e]     = e4m3(code[e]) * scale[e / 128]    (e < 512)
+ *     K_j[512+r] = RoPE value r                      (rope_dim 64 only)
+ *     s_j = sm_scale * sum_d q[t][h][d] * K_j[d], d < 512 + rope_dim
+ *     out[t][h] = sum_j softmax(s)_j * K_j[0..512)
+ *     lse[t][h] = ln sum_j exp(s_j)
+ *   A row with no valid entry gives out = 0 and lse = -inf.  Padding entries
+ *   are never loaded and contribute exactly zero, whatever bytes slot 0 or any
+ *   unreferenced slot holds (NaN codes included).  NoPE (rope_dim 0) scores
+ *   use 512 dims and never read row bytes [528, 656).
+ *
+ * q               bf16 [T][H][512 + rope_dim], contiguous, 16-byte aligned.
+ * kv_cache        uint8 [num_slots][656], 16-byte aligned; num_slots >= 1.
+ * topk_idx        int32 [T][idx_row_stride]; only the first topk_capacity
+ *                 entries of a row are read.  topk_capacity is the buffer's
+ *                 width (e.g. 2176 = index_topk 2048 + a 128-wide tail); the
+ *                 -1 padding bounds the active length.  1 <= topk_capacity <=
+ *                 idx_row_stride.
+ * T, H            1 <= T, 1 <= H <= 128.
+ * rope_dim        64 or 0.
+ * sm_scale        softmax scale (e.g. 1/sqrt(576)), finite.
+ * out             bf16 [T][H][512], 16-byte aligned.
+ * lse             float32 [T][H] natural-log LSE, or NULL.
+ * workspace       device memory of >= sparse_mla_attn_workspace_size(T, H,
+ *                 topk_capacity, rope_dim) bytes (16-byte aligned), or NULL
+ *                 when that size is 0.  Its contents on entry do not matter.
+ */
+int sparse_mla_attn(const void* q,
+                    const void* kv_cache, int64_t num_slots,
+                    const int32_t* topk_idx, int64_t idx_row_stride, int topk_capacity,
+                    int T, int H, int rope_dim, float sm_scale,
+                    void* out, float* lse,
+                    void* workspace, size_t workspace_bytes,
+                    hipStream_t stream);
+
+/* Thread-local description of the last error returned on this thread ("" if none). */
+const char* smla_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_MLA_H */

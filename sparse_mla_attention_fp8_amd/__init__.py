@@ -1,0 +1,126 @@
+"""Python binding of libsparse_mla.so, the MI355X (gfx950) sparse-MLA library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/sparse_mla.h.  torch is used for
+device memory (data_ptr) and the current stream; there is no fallback path,
+and a missing or unloadable library raises.
+
+    kv_write(kv_c, k_pe, slot_mapping, kv_cache)
+    attn(q, kv_cache, topk_idx, sm_scale, rope_dim, topk_capacity=None,
+         out=None, lse=None, workspace=None) -> (out, lse)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsparse_mla.so")
+
+SMLA_OK, SMLA_EINVAL, SMLA_EWORKSPACE, SMLA_ELAUNCH, SMLA_EUNSUPPORTED = 0, -1, -2, -3, -4
+ROW_BYTES = 656
+LATENT = 512
+
+# (name, restype, argtypes) of every exported entry point
+_SIGS = {
+    "mla_kv_write": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]),
+    "sparse_mla_attn_workspace_size": (ctypes.c_size_t, [
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]),
+    "sparse_mla_attn": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "smla_last_error": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+class SparseMLAError(RuntimeError):
+    def __init__(self, call: str, code: int, msg: str):
+        super().__init__(f"{call} returned {code}: {msg}")
+        self.code = code
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m sparse_mla_attention_fp8_amd.build`")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(l, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = l
+    return _lib
+
+
+def _check(call: str, rc: int) -> None:
+    if rc != SMLA_OK:
+        raise SparseMLAError(call, rc, lib().smla_last_error().decode())
+
+
+def _stream(t) -> int:
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def kv_write(kv_c, k_pe, slot_mapping, kv_cache) -> None:
+    """Quantise bf16 rows kv_c [N][>=512] (+ k_pe [N][>=64] or None) into
+    kv_cache uint8 [num_slots][656] at slot_mapping int64 [N]; slot 0 dropped."""
+    import torch
+    assert kv_c.dtype == torch.bfloat16 and kv_c.dim() == 2 and kv_c.stride(1) == 1
+    assert slot_mapping.dtype == torch.int64 and slot_mapping.is_contiguous()
+    assert kv_cache.dtype == torch.uint8 and kv_cache.is_contiguous() and kv_cache.shape[-1] == ROW_BYTES
+    rope_dim = 0
+    pe_stride = 0
+    if k_pe is not None:
+        assert k_pe.dtype == torch.bfloat16 and k_pe.dim() == 2 and k_pe.stride(1) == 1
+        rope_dim, pe_stride = 64, k_pe.stride(0)
+    n = kv_c.shape[0]
+    num_slots = kv_cache.numel() // ROW_BYTES
+    rc = lib().mla_kv_write(kv_c.data_ptr(), kv_c.stride(0), _ptr(k_pe), pe_stride, rope_dim,
+                            slot_mapping.data_ptr(), n, kv_cache.data_ptr(), num_slots,
+                            _stream(kv_cache))
+    _check("mla_kv_write", rc)
+
+
+def workspace_size(T: int, H: int, topk_capacity: int, rope_dim: int) -> int:
+    return int(lib().sparse_mla_attn_workspace_size(T, H, topk_capacity, rope_dim))
+
+
+def attn(q, kv_cache, topk_idx, sm_scale: float, rope_dim: int, topk_capacity: int | None = None,
+         out=None, lse=None, workspace=None, want_lse: bool = True):
+    """Sparse MLA attention.  q bf16 [T][H][512+rope_dim]; kv_cache uint8
+    [num_slots][656]; topk_idx int32 [T][>=W] (row stride may exceed W).
+    Returns (out bf16 [T][H][512], lse float32 [T][H] or None)."""
+    import torch
+    assert q.dtype == torch.bfloat16 and q.dim() == 3 and q.is_contiguous()
+    T, H, D = q.shape
+    assert D == LATENT + rope_dim
+    assert topk_idx.dtype == torch.int32 and topk_idx.dim() == 2 and topk_idx.stride(1) == 1
+    assert kv_cache.dtype == torch.uint8 and kv_cache.is_contiguous()
+    W = topk_idx.shape[1] if topk_capacity is None else int(topk_capacity)
+    if out is None:
+        out = torch.empty((T, H, LATENT), dtype=torch.bfloat16, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    need = workspace_size(T, H, W, rope_dim)
+    if need and (workspace is None or workspace.numel() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().sparse_mla_attn(q.data_ptr(), kv_cache.data_ptr(), kv_cache.numel() // ROW_BYTES,
+                               topk_idx.data_ptr(), topk_idx.stride(0), W, T, H, rope_dim,
+                               float(sm_scale), out.data_ptr(), _ptr(lse), _ptr(workspace),
+                               ws_bytes, _stream(q))
+    _check("sparse_mla_attn", rc)
+    return out, lse

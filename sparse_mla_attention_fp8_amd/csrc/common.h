@@ -1,0 +1,37 @@
+// Shared definitions of the HIP library (device and host side).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace smla {
+
+constexpr int kRowBytes = 656;      // packed fp8_ds_mla row
+constexpr int kLatent = 512;        // latent width = value width
+constexpr int kTile = 128;          // quantisation tile
+constexpr int kScaleOff = 512;      // 4 x float32 tile scales
+constexpr int kRopeOff = 528;       // 64 x bf16 RoPE, or zeros for NoPE rows
+constexpr int kNopeRowBytes = 528;  // bytes a NoPE reader needs
+
+// Internal launchers (return a hipError_t from the launch).
+hipError_t launch_kv_write(const uint16_t* kv_c, int64_t kv_c_stride, const uint16_t* k_pe,
+                           int64_t k_pe_stride, int rope_dim, const int64_t* slot_mapping,
+                           int64_t num_rows, uint8_t* cache, int64_t num_slots,
+                           hipStream_t stream);
+
+// Launch plan of the attention call; a pure function of the sizes, shared by
+// the workspace query and the launch so the two always agree.
+struct AttnPlan {
+  int head_groups;   // ceil(H / 16)
+  int splits;        // split-top-k count per (row, head group)
+  int range;         // top-k entries per split (multiple of the chunk size)
+  size_t workspace;  // bytes of partial results (0 when splits == 1)
+};
+AttnPlan plan_attn(int T, int H, int topk_capacity, int rope_dim);
+
+hipError_t launch_attn(const uint16_t* q, const uint8_t* cache, int64_t num_slots,
+                       const int32_t* idx, int64_t idx_stride, int W, int T, int H,
+                       int rope_dim, float sm_scale, uint16_t* out, float* lse,
+                       void* workspace, const AttnPlan& plan, hipStream_t stream);
+
+}  // namespace smla

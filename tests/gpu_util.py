@@ -1,0 +1,107 @@
+"""Helpers shared by the GPU tests: device copies of workloads, cache builds
+through the HIP writer, and the parity bar against the oracle."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import sparse_mla_attention_fp8_amd as smla
+import workloads as wl
+from oracle import attention as oracle_attn
+from oracle import writer as oracle_writer
+
+DEV = "cuda:0"
+
+# Parity bar for attention outputs: max |o_gpu - o_ref| <= 2e-2 over all
+# elements, per-(row, head) relative L2 <= 1e-2, no NaN/Inf; lse within 1e-3.
+MAX_ABS = 2e-2
+MAX_REL_L2 = 1e-2
+MAX_LSE = 1e-3
+
+
+def bf16_dev(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def build_cache(cfg: dict, check_slots=None) -> torch.Tensor:
+    """Writes every row of the workload through the HIP writer into a zeroed
+    device cache, checks the written bytes against the oracle writer (all rows,
+    or only `check_slots`), then fills slot 0 with the workload's poison."""
+    num_slots = cfg["num_slots"]
+    cache = torch.zeros((num_slots, wl.ROW_BYTES), dtype=torch.uint8, device=DEV)
+    lat = bf16_dev(cfg["latent"])
+    rope = bf16_dev(cfg["rope"]) if cfg["rope"] is not None else None
+    slots = torch.from_numpy(cfg["slots"]).to(DEV)
+    smla.kv_write(lat, rope, slots, cache)
+    torch.cuda.synchronize()
+    if check_slots is None:
+        sel = cfg["slots"]
+    else:
+        sel = np.unique(np.asarray(check_slots, dtype=np.int64))
+        sel = sel[(sel >= 1) & (sel < num_slots)]
+    rows = sel - 1                          # workload row i is written to slot i + 1
+    want = oracle_writer.encode_rows(cfg["latent"][rows],
+                                     None if cfg["rope"] is None else cfg["rope"][rows])
+    got = cache[torch.from_numpy(sel).to(DEV)].cpu().numpy()
+    assert np.array_equal(got, want), "HIP writer bytes differ from the oracle writer"
+    cache[0] = torch.from_numpy(cfg["slot0"]).to(DEV)
+    return cache
+
+
+def oracle_cache(cfg: dict, slots_needed) -> np.ndarray:
+    """A host cache holding oracle-written rows for the needed slots (others 0)
+    and the workload's slot-0 bytes."""
+    cache = np.zeros((cfg["num_slots"], wl.ROW_BYTES), dtype=np.uint8)
+    sel = np.unique(np.asarray(slots_needed, dtype=np.int64))
+    sel = sel[(sel >= 1) & (sel < cfg["num_slots"])]
+    cache[sel] = oracle_writer.encode_rows(cfg["latent"][sel - 1],
+                                           None if cfg["rope"] is None else cfg["rope"][sel - 1])
+    cache[0] = cfg["slot0"]
+    return cache
+
+
+def run_attn(cfg: dict, cache: torch.Tensor, idx: np.ndarray | None = None, W: int | None = None,
+             H: int | None = None, q=None):
+    idx = cfg["idx"] if idx is None else idx
+    W = idx.shape[1] if W is None else W
+    qb = cfg["q"] if q is None else q
+    out, lse = smla.attn(bf16_dev(qb), cache, torch.from_numpy(np.ascontiguousarray(idx)).to(DEV),
+                         cfg["sm_scale"], cfg["rope_dim"], topk_capacity=W)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def oracle_for(cfg: dict, rows, idx: np.ndarray | None = None, W: int | None = None, q=None):
+    idx = cfg["idx"] if idx is None else idx
+    W = idx.shape[1] if W is None else W
+    qb = cfg["q"] if q is None else q
+    need = idx[np.asarray(rows)][:, :W].ravel()
+    cache = oracle_cache(cfg, need[need >= 0])
+    return oracle_attn.sparse_mla_attn(qb, cache, idx, W, cfg["rope_dim"], cfg["sm_scale"],
+                                       rows=list(rows))
+
+
+def assert_parity(out: torch.Tensor, lse: torch.Tensor, ref_out, ref_lse, rows):
+    rows = np.asarray(rows)
+    o = to_f64(out)[rows]
+    r = ref_out[rows]
+    assert np.all(np.isfinite(o)), "non-finite attention output"
+    err = np.abs(o - r)
+    assert err.max() <= MAX_ABS, f"max abs err {err.max():.3e}"
+    num = np.sqrt(((o - r) ** 2).sum(axis=-1))
+    den = np.maximum(np.sqrt((r ** 2).sum(axis=-1)), 1e-30)
+    empty = np.sqrt((r ** 2).sum(axis=-1)) == 0
+    rel = np.where(empty, num, num / den)
+    assert rel.max() <= MAX_REL_L2, f"max row rel L2 {rel.max():.3e}"
+    if lse is not None:
+        g = lse.cpu().numpy().astype(np.float64)[rows]
+        rl = ref_lse[rows]
+        inf = np.isneginf(rl)
+        assert np.array_equal(np.isneginf(g), inf)
+        assert np.all(np.isfinite(g[~inf]))
+        d = np.abs(g[~inf] - rl[~inf])
+        assert d.size == 0 or d.max() <= MAX_LSE, f"lse err {d.max():.3e}"

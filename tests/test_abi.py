@@ -1,0 +1,104 @@
+"""The C-ABI library loads, exports every entry point of include/*.h, and
+rejects bad arguments on the host before any GPU work (no device needed)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import sparse_mla_attention_fp8_amd as smla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert {"mla_kv_write", "sparse_mla_attn", "sparse_mla_attn_workspace_size",
+            "smla_last_error"} <= names
+    raw = ctypes.CDLL(smla.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+    assert set(smla._SIGS) == names
+
+
+FAKE = 0x10000          # an aligned address that is never dereferenced
+
+
+def test_kv_write_validation():
+    L = smla.lib()
+    bad = [
+        dict(rope_dim=5),
+        dict(kv_c=None),
+        dict(slot_mapping=None),
+        dict(kv_cache=None),
+        dict(k_pe=None),                      # rope_dim 64 needs k_pe
+        dict(rope_dim=0),                     # k_pe must be NULL with rope 0
+        dict(kv_c_row_stride=500),
+        dict(kv_c_row_stride=516),
+        dict(k_pe_row_stride=60),
+        dict(kv_c=FAKE + 8),
+        dict(num_rows=-1),
+        dict(num_slots=0),
+    ]
+    base = dict(kv_c=FAKE, kv_c_row_stride=512, k_pe=FAKE, k_pe_row_stride=64, rope_dim=64,
+                slot_mapping=FAKE, num_rows=4, kv_cache=FAKE, num_slots=128, stream=None)
+    for b in bad:
+        a = {**base, **b}
+        rc = L.mla_kv_write(*a.values())
+        assert rc == smla.SMLA_EINVAL, b
+        assert L.smla_last_error().decode().startswith("mla_kv_write")
+    # zero rows is a no-op that launches nothing
+    assert L.mla_kv_write(*{**base, "num_rows": 0}.values()) == smla.SMLA_OK
+
+
+def test_attn_validation():
+    L = smla.lib()
+    base = dict(q=FAKE, kv_cache=FAKE, num_slots=4096, topk_idx=FAKE, idx_row_stride=2176,
+                topk_capacity=2176, T=4, H=16, rope_dim=0, sm_scale=0.04, out=FAKE, lse=None,
+                workspace=None, workspace_bytes=0, stream=None)
+    bad = [
+        (dict(rope_dim=32), smla.SMLA_EINVAL),
+        (dict(T=0), smla.SMLA_EINVAL),
+        (dict(H=0), smla.SMLA_EINVAL),
+        (dict(H=129), smla.SMLA_EINVAL),
+        (dict(topk_capacity=0), smla.SMLA_EINVAL),
+        (dict(idx_row_stride=2048), smla.SMLA_EINVAL),
+        (dict(num_slots=0), smla.SMLA_EINVAL),
+        (dict(q=None), smla.SMLA_EINVAL),
+        (dict(out=None), smla.SMLA_EINVAL),
+        (dict(q=FAKE + 4), smla.SMLA_EINVAL),
+        (dict(sm_scale=float("nan")), smla.SMLA_EINVAL),
+        (dict(T=70000), smla.SMLA_EUNSUPPORTED),
+        (dict(T=4), smla.SMLA_EWORKSPACE),    # 4 rows need split partials
+        (dict(T=4, workspace=FAKE, workspace_bytes=16), smla.SMLA_EWORKSPACE),
+    ]
+    for b, code in bad:
+        a = {**base, **b}
+        rc = L.sparse_mla_attn(*a.values())
+        assert rc == code, (b, rc)
+        assert L.smla_last_error().decode().startswith("sparse_mla_attn")
+
+
+def test_workspace_size():
+    assert smla.workspace_size(0, 16, 2048, 64) == 0
+    assert smla.workspace_size(4, 16, 2048, 77) == 0
+    big = smla.workspace_size(256, 16, 2048, 64)
+    small = smla.workspace_size(1, 16, 2048, 64)
+    assert small > 0
+    # one split per row needs no partials; whatever is returned is a whole number of
+    # fp32 [H][514] records per (row, split)
+    for T in (1, 2, 16, 64, 256):
+        ws = smla.workspace_size(T, 16, 2176, 0)
+        assert ws % (16 * 514 * 4 * T) == 0
+    assert big % (16 * 514 * 4 * 256) == 0

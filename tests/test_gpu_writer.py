@@ -1,0 +1,114 @@
+"""HIP writer vs the oracle writer: byte-exact rows, dropped padding rows,
+untouched bytes, NoPE zero tail, and a sweep of every bf16 value."""
+import numpy as np
+import pytest
+import torch
+
+import sparse_mla_attention_fp8_amd as smla
+import workloads as wl
+from oracle import writer as oracle_writer
+from tests.gpu_util import DEV, bf16_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(cfg, lat=None, rope=None):
+    cache = torch.from_numpy(cfg["cache"]).to(DEV)
+    lat_t = bf16_dev(cfg["latent"]) if lat is None else lat
+    rope_t = (bf16_dev(cfg["rope"]) if cfg["rope"] is not None else None) if rope is None else rope
+    smla.kv_write(lat_t, rope_t, torch.from_numpy(cfg["slots"]).to(DEV), cache)
+    torch.cuda.synchronize()
+    return cache.cpu().numpy()
+
+
+@pytest.mark.parametrize("N", [1024, 8192])
+@pytest.mark.parametrize("rope_dim", [64, 0])
+@pytest.mark.parametrize("shuffle", [False, True])
+def test_writer_workload_byte_exact(N, rope_dim, shuffle):
+    print(f"writer N={N} rope={rope_dim} shuffle={shuffle}", flush=True)
+    cfg = wl.config_writer(N=N, rope_dim=rope_dim, shuffle=shuffle)
+    got = _run(cfg)
+    want = cfg["cache"].copy()
+    keep = oracle_writer.kv_write(want, cfg["latent"], cfg["rope"], cfg["slots"])
+    assert keep.sum() == N - N // 4
+    assert not got[0].any(), "reserved slot 0 was written"
+    if rope_dim == 0:
+        assert not got[cfg["slots"][keep], 528:].any()
+    assert np.array_equal(got, want)
+
+
+def test_every_bf16_value_with_unit_scale():
+    """Each tile holds 448 (so scale = 1 exactly and the quantiser input is x
+    itself) plus 127 bf16 values; all finite bf16 values below 448 in
+    magnitude are covered, which includes every e4m3 rounding tie."""
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    x = (bits << 16).view(np.float32)
+    vals = bits[np.isfinite(x) & (np.abs(x) < 448.0)].astype(np.uint16)
+    n_tiles = (vals.size + 126) // 127
+    tiles = np.zeros((n_tiles, 128), dtype=np.uint16)
+    flat = np.zeros(n_tiles * 127, dtype=np.uint16)
+    flat[: vals.size] = vals
+    tiles[:, 1:] = flat.reshape(n_tiles, 127)
+    tiles[:, 0] = 0x43E0                                   # 448.0
+    n_rows = (n_tiles + 3) // 4
+    lat = np.zeros((n_rows * 4, 128), dtype=np.uint16)
+    lat[:n_tiles] = tiles
+    lat[n_tiles:, 0] = 0x43E0
+    lat = lat.reshape(n_rows, 512)
+    num_slots = n_rows + 1
+    cfg = dict(cache=np.zeros((num_slots, 656), dtype=np.uint8), latent=lat, rope=None,
+               slots=np.arange(1, num_slots, dtype=np.int64))
+    got = _run(cfg)
+    want = cfg["cache"].copy()
+    oracle_writer.kv_write(want, lat, None, cfg["slots"])
+    assert np.array_equal(got, want)
+
+
+def test_scales_across_magnitudes_and_zero_tiles():
+    rng = np.random.default_rng(8)
+    n = 400
+    x = rng.standard_normal((n, 512)).astype(np.float32)
+    x *= np.exp2(rng.integers(-120, 120, size=(n, 1))).astype(np.float32)
+    x[5, 128:256] = 0.0                      # an all-zero tile
+    x[6, 0:128] = -0.0                       # an all negative-zero tile
+    x[7, 256:384] = 0.0
+    x[7, 300] = -1e-30                       # one tiny value in a zero tile
+    lat = wl.bf16_bits_from_f32(x)
+    rope = wl.normal_bf16(rng, (n, 64))
+    cfg = dict(cache=np.full((n + 1, 656), 0x5A, dtype=np.uint8), latent=lat, rope=rope,
+               slots=np.arange(1, n + 1, dtype=np.int64))
+    got = _run(cfg)
+    want = cfg["cache"].copy()
+    oracle_writer.kv_write(want, lat, rope, cfg["slots"])
+    assert np.array_equal(got, want)
+    assert np.all(got[0] == 0x5A)
+
+
+def test_strided_views_of_one_kv_tensor():
+    """kv_c and k_pe as column slices of one [N][576] tensor (row stride 576)."""
+    rng = np.random.default_rng(9)
+    n, num_slots = 777, 5000
+    full = wl.normal_bf16(rng, (n, 576))
+    slots = rng.choice(num_slots - 1, size=n, replace=False).astype(np.int64) + 1
+    slots[::10] = 0
+    t = bf16_dev(full)
+    cfg = dict(cache=np.zeros((num_slots, 656), dtype=np.uint8), latent=full[:, :512],
+               rope=full[:, 512:], slots=slots)
+    got = _run(cfg, lat=t[:, :512], rope=t[:, 512:])
+    want = cfg["cache"].copy()
+    oracle_writer.kv_write(want, full[:, :512], full[:, 512:], slots)
+    assert np.array_equal(got, want)
+
+
+def test_out_of_range_slots_are_dropped():
+    rng = np.random.default_rng(10)
+    num_slots = 100
+    lat = wl.normal_bf16(rng, (6, 512))
+    slots = np.array([-5, 0, 100, 1 << 40, 99, 1], dtype=np.int64)
+    cfg = dict(cache=np.full((num_slots, 656), 0xA5, dtype=np.uint8), latent=lat, rope=None,
+               slots=slots)
+    cfg["cache"][0] = 0
+    got = _run(cfg)
+    want = cfg["cache"].copy()
+    oracle_writer.kv_write(want, lat, None, slots)
+    assert np.array_equal(got, want)
