@@ -39,7 +39,8 @@
 namespace smla {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
 constexpr int kHeads = 16;          // heads per workgroup (MFMA N)
 constexpr int kKeys = 64;           // keys per chunk (4 blocks of 16)
 constexpr int kMaxRange = 2304;     // top-k entries one split may own
@@ -48,6 +49,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef int i8v __attribute__((ext_vector_type(8)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v2i lds_v2i;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
@@ -57,10 +61,7 @@ struct Geo {
   static constexpr int RB = ROPE ? 656 : 528;       // bytes staged per row
   static constexpr int NSEG = RB / 16;              // 16-byte segments per row
   static constexpr int STAGE = kKeys * RB;          // bytes per stage
-  // a chunk is NSEG direct-to-LDS instructions of 64 x 16 B, dealt round-robin
-  // to the 4 wavefronts; wavefront 0 takes the extra one
-  static constexpr int CNT0 = (NSEG + 3) / 4;
-  static constexpr int CNT = NSEG / 4;
+  static constexpr int NST = ROPE ? 3 : 4;          // ring depth: NST - 1 chunks in flight
 };
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] at [15:14])
@@ -145,28 +146,58 @@ __device__ __forceinline__ void tr4x4(uint32_t a0, uint32_t a1, uint32_t a2, uin
   b3 = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
 }
 
+// Reductions over the four lanes l, l^16, l^32, l^48 that hold one head (VALU
+// row swaps; no LDS round trip).
+__device__ __forceinline__ float max_xg(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_xg(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// LDS row read by row m of 16-key block bb of a chunk.  Odd blocks are
+// rotated by 8 rows: the 16 rows of any block still cover all residues mod 16,
+// and the 8 rows a P.V lane group takes from blocks 2s and 2s+1 (rows 4g..4g+3
+// of each) now also differ mod 16.  With row strides of 4 or 36 dwords mod 64
+// banks, rows that differ mod 16 sit on distinct banks.
+__device__ __forceinline__ int key_row(int bb, int m) { return 16 * bb + ((m + 8 * (bb & 1)) & 15); }
+
 __device__ __forceinline__ long pack64(uint32_t lo, uint32_t hi) {
   return (long)(((uint64_t)hi << 32) | lo);
 }
 
-// Compacts the valid entries of idx[lo, hi) into list[] in order; returns the count.
+// Compacts the valid entries of idx[lo, hi) into list[] in order; returns the
+// count.  All index loads are issued before the first round so their latency
+// is paid once.
 __device__ int compact_valid(const int32_t* __restrict__ idx, int lo, int hi, int64_t num_slots,
                              int* list, int* wave_counts) {
+  constexpr int kRounds = (kMaxRange + kThreads - 1) / kThreads;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int v[kRounds];
+#pragma unroll
+  for (int i = 0; i < kRounds; ++i) {
+    const int k = lo + i * kThreads + tid;
+    v[i] = k < hi ? idx[k] : -1;
+  }
   int total = 0;
-  for (int base = lo; base < hi; base += kThreads) {
-    const int k = base + tid;
-    int v = -1;
-    if (k < hi) v = idx[k];
-    const bool ok = (k < hi) && v >= 0 && (int64_t)v < num_slots;
+#pragma unroll
+  for (int i = 0; i < kRounds; ++i) {
+    if (lo + i * kThreads >= hi) break;
+    const bool ok = v[i] >= 0 && (int64_t)v[i] < num_slots;
     const uint64_t mask = __ballot(ok);
     const int before = __popcll(mask & ((1ull << lane) - 1ull));
     if (lane == 0) wave_counts[wave] = __popcll(mask);
     __syncthreads();
     int off = total;
     for (int w = 0; w < wave; ++w) off += wave_counts[w];
-    if (ok) list[off + before] = v;
-    total += wave_counts[0] + wave_counts[1] + wave_counts[2] + wave_counts[3];
+    if (ok) list[off + before] = v[i];
+    for (int w = 0; w < kWaves; ++w) total += wave_counts[w];
     __syncthreads();
   }
   return total;
@@ -179,44 +210,41 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
     int range, int splits, int head_groups, uint16_t* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ part_o, float* __restrict__ part_ml) {
   using G = Geo<ROPE>;
-  constexpr int D = G::D, RB = G::RB, NSEG = G::NSEG;
+  constexpr int D = G::D, RB = G::RB;
 
-  __shared__ __align__(16) uint8_t st0[G::STAGE];
-  __shared__ __align__(16) uint8_t st1[G::STAGE];
-  __shared__ __align__(16) uint8_t st2[G::STAGE];
+  __shared__ __align__(16) uint8_t stages[G::NST * G::STAGE];   // ring of 64-row stages
   __shared__ int slot_list[kMaxRange];
-  __shared__ __align__(16) float4 pex[4][4][64];   // [tile][block][lane] -> p*scale_tile, keys 4g+r
-  __shared__ float mex[4][kHeads];                  // block max (log2 units)
-  __shared__ float lex[4][kHeads];                  // block sum
-  __shared__ int wave_counts[4];
+  __shared__ __align__(16) float4 xs[4][2][64];   // [block][dim half][lane]: partial scores, keys 4g+r
+  __shared__ int wave_counts[kWaves];
 
   const int tid = threadIdx.x, lane = tid & 63;
   // wave-uniform values are made visibly uniform so that every barrier sits on
   // scalar control flow
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n16 = lane & 15, g = lane >> 4;
+  // QK role: 16 keys (block qb) x 256 dims (half qh, tiles 2qh and 2qh+1) plus
+  // RoPE k-step qh.  P.V role: tile pt, key half ps (keys 32ps..32ps+31 of
+  // each chunk); each key half keeps its own online-softmax state.
+  const int qb = wave >> 1, qh = wave & 1;
+  const int pt = wave >> 1, ps = wave & 1;
   int b = blockIdx.x;
   const int split = b % splits;
   b /= splits;
   const int hg = b % head_groups;
   const int t = b / head_groups;
 
-  // ---- q fragments of head n16 (issued before the index scan) ------------
+  // ---- q fragments of head n16 (issued before the index scan) -------------
   const int head = hg * kHeads + n16;
   const bool hvalid = head < H;
   const uint16_t* qrow = q + ((int64_t)t * H + (hvalid ? head : 0)) * D;
-  uint4 qraw[16];   // k-step 2s+h: dims 64s + 16g + 8h + [0, 8)
+  uint4 qraw[8];    // tile 2qh+u: dims 128(2qh+u) + 32g + 8k + [0, 8), k = 0..3 -> qraw[4u + k]
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    qraw[2 * s] = *reinterpret_cast<const uint4*>(qrow + 64 * s + 16 * g);
-    qraw[2 * s + 1] = *reinterpret_cast<const uint4*>(qrow + 64 * s + 16 * g + 8);
-  }
-  uint4 qpe_raw[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
-  if (ROPE) {
+  for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-      qpe_raw[u] = *reinterpret_cast<const uint4*>(qrow + kLatent + 32 * u + 8 * g);
-  }
+    for (int k = 0; k < 4; ++k)
+      qraw[4 * u + k] = *reinterpret_cast<const uint4*>(qrow + 128 * (2 * qh + u) + 32 * g + 8 * k);
+  uint4 qpe_raw = make_uint4(0, 0, 0, 0);    // RoPE k-step qh: dims 512 + 32qh + 8g + [0, 8)
+  if (ROPE) qpe_raw = *reinterpret_cast<const uint4*>(qrow + kLatent + 32 * qh + 8 * g);
 
   const int lo_k = split * range;
   const int hi_k = min(W, lo_k + range);
@@ -224,10 +252,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
       compact_valid(idx + (int64_t)t * idx_stride, lo_k, hi_k, num_slots, slot_list, wave_counts));
   const int nch = (n + kKeys - 1) / kKeys;
 
-  // ---- q -> e4m3 high + residual, prescaled by a power of two -------------
+  if (!hvalid) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qraw[i] = make_uint4(0, 0, 0, 0);
+    qpe_raw = make_uint4(0, 0, 0, 0);
+  }
+  // ---- q half -> e4m3 high + residual after a per-(head, half) power of two
   float amax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < 8; ++i) {
     const uint32_t w4[4] = {qraw[i].x, qraw[i].y, qraw[i].z, qraw[i].w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -235,259 +268,278 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
       amax = fmaxf(amax, fabsf(__uint_as_float(w4[j] & 0xFFFF0000u)));
     }
   }
-  amax = fmaxf(amax, __shfl_xor(amax, 16));
-  amax = fmaxf(amax, __shfl_xor(amax, 32));
-  // amax * 2^a < 256 with a = 134 - biased exponent of amax
-  int qe = 0;
+  amax = max_xg(amax);
+  int qe = 0;   // amax * 2^qe < 256
   if (amax > 0.0f) {
     qe = 134 - (int)((__float_as_uint(amax) >> 23) & 0xFF);
     qe = qe > 126 ? 126 : (qe < -126 ? -126 : qe);
   }
   const float qscale = exp2_pow(qe);
   const float qinv = exp2_pow(-qe);
-  long qhi[16], qlo[16];
-  if (!hvalid) {
+  i8v qhi[2], qlo[2];   // B operands of v_mfma_f32_16x16x128_f8f6f4, one per tile
 #pragma unroll
-    for (int i = 0; i < 16; ++i) qraw[i] = make_uint4(0, 0, 0, 0);
-    qpe_raw[0] = qpe_raw[1] = make_uint4(0, 0, 0, 0);
-  }
+  for (int u = 0; u < 2; ++u) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t w4[4] = {qraw[i].x, qraw[i].y, qraw[i].z, qraw[i].w};
-    float x[8];
+    for (int k = 0; k < 4; ++k) {
+      const uint4 w = qraw[4 * u + k];
+      const uint32_t w4[4] = {w.x, w.y, w.z, w.w};
+      float x[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      x[2 * j] = __uint_as_float(w4[j] << 16) * qscale;
-      x[2 * j + 1] = __uint_as_float(w4[j] & 0xFFFF0000u) * qscale;
+      for (int j = 0; j < 4; ++j) {
+        x[2 * j] = __uint_as_float(w4[j] << 16) * qscale;
+        x[2 * j + 1] = __uint_as_float(w4[j] & 0xFFFF0000u) * qscale;
+      }
+      uint32_t h0, l0, h1, l1;
+      split_e4m3(x[0], x[1], x[2], x[3], h0, l0);
+      split_e4m3(x[4], x[5], x[6], x[7], h1, l1);
+      qhi[u][2 * k] = (int)h0; qhi[u][2 * k + 1] = (int)h1;
+      qlo[u][2 * k] = (int)l0; qlo[u][2 * k + 1] = (int)l1;
     }
-    uint32_t h0, l0, h1, l1;
-    split_e4m3(x[0], x[1], x[2], x[3], h0, l0);
-    split_e4m3(x[4], x[5], x[6], x[7], h1, l1);
-    qhi[i] = pack64(h0, h1);
-    qlo[i] = pack64(l0, l1);
   }
-  bf16x8 qpe[2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) qpe[u] = __builtin_bit_cast(bf16x8, qpe_raw[u]);
+  const bf16x8 qpe = __builtin_bit_cast(bf16x8, qpe_raw);
 
-  // ---- gather geometry: instruction i = wave + 4j covers flat segments 64i + lane
-  const int my_cnt = wave == 0 ? G::CNT0 : G::CNT;
-  int seg_row[G::CNT0];
-  int seg_off[G::CNT0];
+  // ---- gather geometry: instruction i = wave + 8j covers flat segments 64i + lane
+  constexpr int CNT0 = (G::NSEG + kWaves - 1) / kWaves;
+  constexpr int CNT1 = G::NSEG / kWaves;
+  const bool big = wave < G::NSEG % kWaves;      // issues CNT0 instructions, else CNT1
+  const int my_cnt = big ? CNT0 : CNT1;
+  // row and byte offset of each of this lane's segments (fixed for the kernel)
+  int seg_row[CNT0], seg_off[CNT0];
 #pragma unroll
-  for (int j = 0; j < G::CNT0; ++j) {
-    const int f = 64 * (wave + 4 * j) + lane;
-    seg_row[j] = f / NSEG;
-    seg_off[j] = (f % NSEG) * 16;
+  for (int j = 0; j < CNT0; ++j) {
+    const int f = 64 * (wave + kWaves * j) + lane;
+    seg_row[j] = f / G::NSEG;
+    seg_off[j] = (f - seg_row[j] * G::NSEG) * 16;
   }
   auto issue = [&](uint32_t stage, int c) {
     const int base = c * kKeys;
     const int nv = min(kKeys, n - base);
     const int first = slot_list[base];
 #pragma unroll
-    for (int j = 0; j < G::CNT0; ++j) {
+    for (int j = 0; j < CNT0; ++j) {
       if (j < my_cnt) {
         const int r = seg_row[j];
         const int slot = r < nv ? slot_list[base + r] : first;
         const uint8_t* src = cache + (int64_t)slot * kRowBytes + seg_off[j];
-        dma16(src, stage + 1024u * (uint32_t)(wave + 4 * j));
+        dma16(src, stage + 1024u * (uint32_t)(wave + kWaves * j));
       }
     }
   };
 
-  float m_run = -INFINITY, l_run = 0.0f;
+  float m_run = -INFINITY;   // running max (log2 units) of this key half, per head
+  float l_run = 0.0f;        // running sum over this lane's keys (4g + r)
+  int ne_run = 8;            // oacc = O * 2^(8 - ne_run)
+  int ne_hi = -126;
   f4 oacc[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) oacc[c] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  auto compute = [&](const uint8_t* stg, int c) {
+  auto compute = [&](const uint8_t* stg, int c, uint32_t nxt2) {
     const int nv = min(kKeys, n - c * kKeys);
-    // ---------------- QK^T for keys 16*wave + [0, 16) ----------------
-    const uint8_t* krow = stg + (16 * wave + n16) * RB;
-    f4 acc[4];
-#pragma unroll
-    for (int tl = 0; tl < 4; ++tl) acc[tl] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const uint4 a = *reinterpret_cast<const uint4*>(krow + 64 * s + 16 * g);
-      const int tl = s >> 1;
-      acc[tl] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(pack64(a.x, a.y), qhi[2 * s], acc[tl], 0, 0, 0);
-      acc[tl] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(pack64(a.x, a.y), qlo[2 * s], acc[tl], 0, 0, 0);
-      acc[tl] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(pack64(a.z, a.w), qhi[2 * s + 1], acc[tl], 0, 0, 0);
-      acc[tl] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(pack64(a.z, a.w), qlo[2 * s + 1], acc[tl], 0, 0, 0);
-    }
-    f4 accr = f4{0.0f, 0.0f, 0.0f, 0.0f};
-    if (ROPE) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + kRopeOff + 64 * u + 16 * g);
-        accr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qpe[u], accr, 0, 0, 0);
+    // ---------------- QK^T partial: keys 16qb + [0,16), dims half qh ----------------
+    {
+      const uint8_t* krow = stg + key_row(qb, n16) * RB;
+      f4 acc0 = f4{0.0f, 0.0f, 0.0f, 0.0f}, acc1 = acc0, accr = acc0;
+      {
+        const uint4 p0 = *reinterpret_cast<const uint4*>(krow + 256 * qh + 32 * g);
+        const uint4 p1 = *reinterpret_cast<const uint4*>(krow + 256 * qh + 32 * g + 16);
+        const i8v a = {(int)p0.x, (int)p0.y, (int)p0.z, (int)p0.w, (int)p1.x, (int)p1.y, (int)p1.z, (int)p1.w};
+        acc0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qhi[0], acc0, 0, 0, 0, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qlo[0], acc0, 0, 0, 0, 0, 0, 0);
       }
-    }
-    // lane (head n16, g) holds keys 16*wave + 4g + r, r = 0..3
-    float4 sc[4];
-    float sv[4];
+      {
+        const uint4 p0 = *reinterpret_cast<const uint4*>(krow + 256 * qh + 128 + 32 * g);
+        const uint4 p1 = *reinterpret_cast<const uint4*>(krow + 256 * qh + 128 + 32 * g + 16);
+        const i8v a = {(int)p0.x, (int)p0.y, (int)p0.z, (int)p0.w, (int)p1.x, (int)p1.y, (int)p1.z, (int)p1.w};
+        acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qhi[1], acc1, 0, 0, 0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qlo[1], acc1, 0, 0, 0, 0, 0, 0);
+      }
+      if (ROPE) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + kRopeOff + 64 * qh + 16 * g);
+        accr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qpe, accr, 0, 0, 0);
+      }
+      // chunk c + NST - 1 into the stage everyone finished before the barrier
+      if (c + G::NST - 1 < nch) issue(nxt2, c + G::NST - 1);
+      float pr[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = 16 * wave + 4 * g + r;
-      sc[r] = *reinterpret_cast<const float4*>(stg + key * RB + kScaleOff);
-      const float dot = qinv * (sc[r].x * acc[0][r] + sc[r].y * acc[1][r] +
-                                sc[r].z * acc[2][r] + sc[r].w * acc[3][r]) + accr[r];
-      sv[r] = key < nv ? dot * sm_scale_log2 : -INFINITY;
-    }
-    float mb = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    mb = fmaxf(mb, __shfl_xor(mb, 16));
-    mb = fmaxf(mb, __shfl_xor(mb, 32));
-    float p[4];
-    float lb = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      p[r] = (16 * wave + 4 * g + r < nv) ? __builtin_amdgcn_exp2f(sv[r] - mb) : 0.0f;
-      lb += p[r];
-    }
-    lb += __shfl_xor(lb, 16);
-    lb += __shfl_xor(lb, 32);
-    pex[0][wave][lane] = make_float4(p[0] * sc[0].x, p[1] * sc[1].x, p[2] * sc[2].x, p[3] * sc[3].x);
-    pex[1][wave][lane] = make_float4(p[0] * sc[0].y, p[1] * sc[1].y, p[2] * sc[2].y, p[3] * sc[3].y);
-    pex[2][wave][lane] = make_float4(p[0] * sc[0].z, p[1] * sc[1].z, p[2] * sc[2].z, p[3] * sc[3].z);
-    pex[3][wave][lane] = make_float4(p[0] * sc[0].w, p[1] * sc[1].w, p[2] * sc[2].w, p[3] * sc[3].w);
-    if (g == 0) {
-      mex[wave][n16] = mb;
-      lex[wave][n16] = lb;
+      for (int r = 0; r < 4; ++r) {
+        const float2 sc = *reinterpret_cast<const float2*>(stg + key_row(qb, 4 * g + r) * RB +
+                                                           kScaleOff + 8 * qh);
+        pr[r] = qinv * (sc.x * acc0[r] + sc.y * acc1[r]) + accr[r];
+      }
+      xs[qb][qh][lane] = make_float4(pr[0], pr[1], pr[2], pr[3]);
     }
     lds_barrier();
 
-    // ---------------- softmax state ----------------
-    float mbs[4], fb[4];
+    // ---------------- softmax over keys 32ps + [0,32) ----------------
+    if (nv <= 32 * ps) return;          // no valid key in this half of the chunk
+    float sv[8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) mbs[k] = mex[k][n16];
-    const float m_new = fmaxf(fmaxf(fmaxf(m_run, mbs[0]), mbs[1]), fmaxf(mbs[2], mbs[3]));
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    float lsum = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      fb[k] = __builtin_amdgcn_exp2f(mbs[k] - m_new);       // empty block: -inf -> 0
-      lsum += fb[k] * lex[k][n16];
+    for (int bb = 0; bb < 2; ++bb) {
+      const float4 u0 = xs[2 * ps + bb][0][lane];
+      const float4 u1 = xs[2 * ps + bb][1][lane];
+      sv[4 * bb + 0] = (u0.x + u1.x) * sm_scale_log2;
+      sv[4 * bb + 1] = (u0.y + u1.y) * sm_scale_log2;
+      sv[4 * bb + 2] = (u0.z + u1.z) * sm_scale_log2;
+      sv[4 * bb + 3] = (u0.w + u1.w) * sm_scale_log2;
     }
-    l_run = l_run * alpha + lsum;
+    if (nv < kKeys) {                   // last chunk: padding rows score -inf
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (key_row(2 * ps + (e >> 2), 4 * g + (e & 3)) >= nv) sv[e] = -INFINITY;
+    }
+    float mloc = sv[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mloc = fmaxf(mloc, sv[e]);
+    mloc = max_xg(mloc);                // finite: row 32ps is valid
+    // Lazy running max: it moves only when a score exceeds it by more than
+    // 2^8, so p <= 256 and most chunks leave O's scale untouched.
+    const float m_new = mloc > m_run + 8.0f ? mloc : m_run;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 1 unless m moved
+    float p[8];
+    float psum = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      p[e] = __builtin_amdgcn_exp2f(sv[e] - m_new);   // -inf -> exactly 0
+      psum += p[e];
+    }
+    l_run = l_run * alpha + psum;
     m_run = m_new;
 
-    // ---------------- P.V for latent tile `wave` ----------------
-    float x[2][8];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const float4 v0 = pex[wave][2 * s][lane];
-      const float4 v1 = pex[wave][2 * s + 1][lane];
-      const float f0 = fb[2 * s], f1 = fb[2 * s + 1];
-      x[s][0] = v0.x * f0; x[s][1] = v0.y * f0; x[s][2] = v0.z * f0; x[s][3] = v0.w * f0;
-      x[s][4] = v1.x * f1; x[s][5] = v1.y * f1; x[s][6] = v1.z * f1; x[s][7] = v1.w * f1;
-    }
+    // ---------------- P.V for tile pt ----------------
+    float x[8];
     float nm = 0.0f;
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) nm = fmaxf(nm, x[s][e]);
-    nm = fmaxf(nm, __shfl_xor(nm, 16));
-    nm = fmaxf(nm, __shfl_xor(nm, 32));
-    // power of two N2 >= nm; operands scaled into [0, 256]
+    for (int e = 0; e < 8; ++e) {
+      const float sc = *reinterpret_cast<const float*>(stg + key_row(2 * ps + (e >> 2), 4 * g + (e & 3)) * RB +
+                                                       kScaleOff + 4 * pt);
+      x[e] = p[e] * sc;             // padding rows: p = 0, sc finite (a copied row)
+      nm = fmaxf(nm, x[e]);
+    }
+    nm = max_xg(nm);
+    // power of two 2^ne >= nm; operands scaled into [0, 256].  oacc holds
+    // O * 2^(8 - ne_run); the normaliser follows each chunk but stays within
+    // 2^96 of the largest one seen, which bounds oacc by 2^(11+9+8+96) < 2^128.
     int ne = 0;
     if (nm > 0.0f) {
       const uint32_t bits = __float_as_uint(nm);
       ne = (int)((bits >> 23) & 0xFF) - 127 + ((bits & 0x7FFFFF) ? 1 : 0);
-      ne = ne > 119 ? 119 : (ne < -126 ? -126 : ne);
+      ne = ne > 119 ? 119 : (ne < -118 ? -118 : ne);
     }
+    ne_hi = ne > ne_hi ? ne : ne_hi;
+    ne = ne < ne_hi - 96 ? ne_hi - 96 : ne;
+    // keep the previous normaliser unless the chunk would exceed 256 or sit
+    // more than 8 binades below it
+    if (ne <= ne_run && ne >= ne_run - 8) ne = ne_run;
     const float inv = exp2_pow(8 - ne);
-    const float post = exp2_pow(ne - 8);
-    long bhi[2], blo[2];
+    const float resc = ldexpf(alpha, ne_run - ne);
+    ne_run = ne;
+    if (!__all(resc == 1.0f)) {
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      uint32_t h0, l0, h1, l1;
-      split_e4m3(x[s][0] * inv, x[s][1] * inv, x[s][2] * inv, x[s][3] * inv, h0, l0);
-      split_e4m3(x[s][4] * inv, x[s][5] * inv, x[s][6] * inv, x[s][7] * inv, h1, l1);
-      bhi[s] = pack64(h0, h1);
-      blo[s] = pack64(l0, l1);
+      for (int cc = 0; cc < 8; ++cc)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) oacc[cc][r] *= resc;
     }
-    f4 tacc[8];
+    uint32_t h0, l0, h1, l1;
+    split_e4m3(x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv, h0, l0);
+    split_e4m3(x[4] * inv, x[5] * inv, x[6] * inv, x[7] * inv, h1, l1);
+    const long bhi = pack64(h0, h1), blo = pack64(l0, l1);
+    // V^T through the LDS transpose read: within each 16-lane group, source
+    // lane 2k+h reads 8 bytes of slot k's row at dims d0 + 8h; lane i then holds
+    // dim d0 + i of the group's 8 slots (byte k = slot k), the A operand of
+    // one 16-dim block.
+    const int k8 = n16 >> 1, h8 = n16 & 1;
+    const uint8_t* vsrc = stg + key_row(2 * ps + (k8 >> 2), 4 * g + (k8 & 3)) * RB + 128 * pt + 8 * h8;
 #pragma unroll
-    for (int cc = 0; cc < 8; ++cc) tacc[cc] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      uint2 v[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int key = 32 * s + 16 * (e >> 2) + 4 * g + (e & 3);
-        v[e] = *reinterpret_cast<const uint2*>(stg + key * RB + 128 * wave + 8 * n16);
-      }
-      uint32_t lo[8], hi[8];
-      tr4x4(v[0].x, v[1].x, v[2].x, v[3].x, lo[0], lo[1], lo[2], lo[3]);
-      tr4x4(v[4].x, v[5].x, v[6].x, v[7].x, hi[0], hi[1], hi[2], hi[3]);
-      tr4x4(v[0].y, v[1].y, v[2].y, v[3].y, lo[4], lo[5], lo[6], lo[7]);
-      tr4x4(v[4].y, v[5].y, v[6].y, v[7].y, hi[4], hi[5], hi[6], hi[7]);
-#pragma unroll
-      for (int cc = 0; cc < 8; ++cc) {
-        const long a = pack64(lo[cc], hi[cc]);
-        tacc[cc] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, bhi[s], tacc[cc], 0, 0, 0);
-        tacc[cc] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, blo[s], tacc[cc], 0, 0, 0);
-      }
+    for (int cc = 0; cc < 8; ++cc) {
+      const v2i tv = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(vsrc + 16 * cc));
+      const long a = pack64((uint32_t)tv[0], (uint32_t)tv[1]);
+      oacc[cc] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, bhi, oacc[cc], 0, 0, 0);
+      oacc[cc] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, blo, oacc[cc], 0, 0, 0);
     }
-#pragma unroll
-    for (int cc = 0; cc < 8; ++cc)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) oacc[cc][r] = oacc[cc][r] * alpha + tacc[cc][r] * post;
   };
 
-  // ---- pipeline: chunk c lives in stage c % 3; two chunks in flight -------
-  const uint32_t a0 = lds_addr(st0), a1 = lds_addr(st1), a2 = lds_addr(st2);
+  // ---- pipeline: chunk c lives in stage c % NST; NST - 1 chunks in flight ----
+  const uint32_t lds0 = lds_addr(stages);
   // Every compiler-visible load (q) is complete before the pipeline starts, so
   // the compiler has no reason to emit a vmcnt wait of its own in the loop
   // (it does not count the inline-asm gathers; a wait of its own there would
   // drain the whole pipeline).
   __builtin_amdgcn_s_waitcnt(0);
-  if (nch > 0) issue(a0, 0);
-  if (nch > 1) issue(a1, 1);
-  auto step = [&](const uint8_t* cur, uint32_t nxt2, int c) {
-    if (c + 1 < nch) {
-      if (wave == 0) vm_barrier<G::CNT0>(); else vm_barrier<G::CNT>();
-    } else {
+#pragma unroll
+  for (int c = 0; c < G::NST - 1; ++c)
+    if (c < nch) issue(lds0 + (uint32_t)(c * G::STAGE), c);
+  int cur = 0;                       // stage of chunk c
+  for (int c = 0; c < nch; ++c) {
+    // this wave's gathers issued after chunk c's: those of chunks c+1 .. c+NST-2
+    const int ahead = min(G::NST - 2, nch - 1 - c);
+    if (ahead <= 0) {
       vm_barrier<0>();
+    } else if (ahead == 1) {
+      if (big) vm_barrier<CNT0>(); else vm_barrier<CNT1>();
+    } else {
+      if (big) vm_barrier<2 * CNT0>(); else vm_barrier<2 * CNT1>();
     }
-    if (c + 2 < nch) issue(nxt2, c + 2);
-    compute(cur, c);
-  };
-  for (int c = 0; c < nch; c += 3) {
-    step(st0, a2, c);
-    if (c + 1 < nch) step(st1, a0, c + 1);
-    if (c + 2 < nch) step(st2, a1, c + 2);
+    const int nxt = cur == 0 ? G::NST - 1 : cur - 1;   // stage of chunk c + NST - 1
+    compute(stages + cur * G::STAGE, c, lds0 + (uint32_t)(nxt * G::STAGE));
+    cur = cur == G::NST - 1 ? 0 : cur + 1;
   }
 
-  // ---- epilogue ----------------------------------------------------------
-  if (!hvalid) return;
-  const int dim0 = 128 * wave + 32 * g;   // lane's dims: dim0 + 8r + c
+  // ---- combine the two key halves, then write ------------------------------
+  const float l_full = sum_xg(l_run);
+  const float post = exp2_pow(ne_run - 8);
+#pragma unroll
+  for (int cc = 0; cc < 8; ++cc)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) oacc[cc][r] *= post;
+  lds_barrier();                       // every wave is done with the stages
+  float4* mo = reinterpret_cast<float4*>(stages);              // [c][pt][lane] partial O (32 KB)
+  float2* ml = reinterpret_cast<float2*>(stages + 4 * 64 * 128);  // [pt][lane] (m, l)
+  const int slot4 = pt * 64 + lane;
+  if (ps == 1) {
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc)
+      mo[cc * 256 + slot4] = make_float4(oacc[cc][0], oacc[cc][1], oacc[cc][2], oacc[cc][3]);
+    ml[slot4] = make_float2(m_run, l_full);
+  }
+  lds_barrier();
+  if (ps == 1 || !hvalid) return;
+  const float2 o1 = ml[slot4];
+  const float M = fmaxf(m_run, o1.x);
+  const float w0 = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - M);
+  const float w1 = o1.x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(o1.x - M);
+  const float L = w0 * l_full + w1 * o1.y;
+  // oacc[c][r] (and mo) hold dim 128pt + 16c + 4g + r
+  const int dim0 = 128 * pt + 4 * g;
   if (splits == 1) {
-    const float il = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+    const float il = L > 0.0f ? 1.0f / L : 0.0f;
     uint16_t* dst = out + ((int64_t)t * H + head) * kLatent + dim0;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      uint32_t pk[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        pk[k] = (uint32_t)f32_to_bf16_rne(oacc[2 * k][r] * il) |
-                ((uint32_t)f32_to_bf16_rne(oacc[2 * k + 1][r] * il) << 16);
-      *reinterpret_cast<uint4*>(dst + 8 * r) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    for (int cc = 0; cc < 8; ++cc) {
+      const float4 u = mo[cc * 256 + slot4];
+      const float o4[4] = {w0 * oacc[cc][0] + w1 * u.x, w0 * oacc[cc][1] + w1 * u.y,
+                           w0 * oacc[cc][2] + w1 * u.z, w0 * oacc[cc][3] + w1 * u.w};
+      const uint32_t lo2 = (uint32_t)f32_to_bf16_rne(o4[0] * il) |
+                           ((uint32_t)f32_to_bf16_rne(o4[1] * il) << 16);
+      const uint32_t hi2 = (uint32_t)f32_to_bf16_rne(o4[2] * il) |
+                           ((uint32_t)f32_to_bf16_rne(o4[3] * il) << 16);
+      *reinterpret_cast<uint2*>(dst + 16 * cc) = make_uint2(lo2, hi2);
     }
-    if (lse != nullptr && wave == 0 && g == 0)
-      lse[(int64_t)t * H + head] = l_run > 0.0f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
+    if (lse != nullptr && pt == 0 && g == 0)
+      lse[(int64_t)t * H + head] = L > 0.0f ? (M + __log2f(L)) * kLn2 : -INFINITY;
   } else {
-    const int64_t p = ((int64_t)t * splits + split) * H + head;
-    float* dst = part_o + p * kLatent + dim0;
+    const int64_t pidx = ((int64_t)t * splits + split) * H + head;
+    float* dst = part_o + pidx * kLatent + dim0;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      *reinterpret_cast<float4*>(dst + 8 * r) = make_float4(oacc[0][r], oacc[1][r], oacc[2][r], oacc[3][r]);
-      *reinterpret_cast<float4*>(dst + 8 * r + 4) = make_float4(oacc[4][r], oacc[5][r], oacc[6][r], oacc[7][r]);
+    for (int cc = 0; cc < 8; ++cc) {
+      const float4 u = mo[cc * 256 + slot4];
+      *reinterpret_cast<float4*>(dst + 16 * cc) =
+          make_float4(w0 * oacc[cc][0] + w1 * u.x, w0 * oacc[cc][1] + w1 * u.y,
+                      w0 * oacc[cc][2] + w1 * u.z, w0 * oacc[cc][3] + w1 * u.w);
     }
-    if (wave == 0 && g == 0) {
-      part_ml[2 * p] = m_run;
-      part_ml[2 * p + 1] = l_run;
+    if (pt == 0 && g == 0) {
+      part_ml[2 * pidx] = M;
+      part_ml[2 * pidx + 1] = L;
     }
   }
 }
