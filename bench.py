@@ -36,7 +36,31 @@ def _args():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-extras", action="store_true", help="headline step only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run plain device copies of 512 MiB (to scale HBM byte counters)")
     return ap.parse_args()
+
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_nope_T256_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "sparse_mla_attention_fp8_amd", "csrc", "attn.hip")
+
+
+def kernel_source_sha256() -> str:
+    import hashlib
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the headline attention kernel from the committed
+    counter summary, or None when it is missing or was taken on other source."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != kernel_source_sha256():
+        return None
+    return rec
 
 
 def main():
@@ -48,6 +72,14 @@ def main():
         sys.exit(2)
 
     import torch
+    if a.calibrate_copy:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": src.numel(), "launches": 5}), flush=True)
+        return
     import sparse_mla_attention_fp8_amd as smla
     import workloads as wl
 
@@ -187,6 +219,12 @@ def main():
         "traffic": None,
         "kernel": "sparse_mla_attn main kernel, NoPE T=256 (one split per row, no merge)",
     }
+    tr = measured_traffic()
+    if tr is not None:
+        result["roofline"]["traffic"] = tr["hbm_bytes_per_launch"]
+        result["roofline"]["traffic_detail"] = {k: tr[k] for k in
+                                                ("fetch_bytes_per_launch", "write_bytes_per_launch",
+                                                 "copy_scale_fetch", "copy_scale_write")}
     del caches
 
     extras = {}
