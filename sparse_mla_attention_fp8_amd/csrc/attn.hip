@@ -314,13 +314,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
   auto issue = [&](uint32_t stage, int c) {
     const int base = c * kKeys;
     const int nv = min(kKeys, n - base);
-    const int first = slot_list[base];
+    // all slot lookups first (rows past the valid count take the chunk's first
+    // row), so the loads below do not each wait on an LDS round trip
+    int slot[CNT0];
+#pragma unroll
+    for (int j = 0; j < CNT0; ++j) slot[j] = slot_list[base + (seg_row[j] < nv ? seg_row[j] : 0)];
 #pragma unroll
     for (int j = 0; j < CNT0; ++j) {
       if (j < my_cnt) {
-        const int r = seg_row[j];
-        const int slot = r < nv ? slot_list[base + r] : first;
-        const uint8_t* src = cache + (int64_t)slot * kRowBytes + seg_off[j];
+        const uint8_t* src = cache + (int64_t)slot[j] * kRowBytes + seg_off[j];
         dma16(src, stage + 1024u * (uint32_t)(wave + kWaves * j));
       }
     }
@@ -339,25 +341,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
     // ---------------- QK^T partial: keys 16qb + [0,16), dims half qh ----------------
     {
       const uint8_t* krow = stg + key_row(qb, n16) * RB;
-      f4 acc0 = f4{0.0f, 0.0f, 0.0f, 0.0f}, acc1 = acc0, accr = acc0;
-      {
-        const uint4 p0 = *reinterpret_cast<const uint4*>(krow + 256 * qh + 32 * g);
-        const uint4 p1 = *reinterpret_cast<const uint4*>(krow + 256 * qh + 32 * g + 16);
-        const i8v a = {(int)p0.x, (int)p0.y, (int)p0.z, (int)p0.w, (int)p1.x, (int)p1.y, (int)p1.z, (int)p1.w};
-        acc0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qhi[0], acc0, 0, 0, 0, 0, 0, 0);
-        acc0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qlo[0], acc0, 0, 0, 0, 0, 0, 0);
-      }
-      {
-        const uint4 p0 = *reinterpret_cast<const uint4*>(krow + 256 * qh + 128 + 32 * g);
-        const uint4 p1 = *reinterpret_cast<const uint4*>(krow + 256 * qh + 128 + 32 * g + 16);
-        const i8v a = {(int)p0.x, (int)p0.y, (int)p0.z, (int)p0.w, (int)p1.x, (int)p1.y, (int)p1.z, (int)p1.w};
-        acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qhi[1], acc1, 0, 0, 0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qlo[1], acc1, 0, 0, 0, 0, 0, 0);
-      }
-      if (ROPE) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + kRopeOff + 64 * qh + 16 * g);
-        accr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qpe, accr, 0, 0, 0);
-      }
+      const uint4 p00 = *reinterpret_cast<const uint4*>(krow + 256 * qh + 32 * g);
+      const uint4 p01 = *reinterpret_cast<const uint4*>(krow + 256 * qh + 32 * g + 16);
+      const uint4 p10 = *reinterpret_cast<const uint4*>(krow + 256 * qh + 128 + 32 * g);
+      const uint4 p11 = *reinterpret_cast<const uint4*>(krow + 256 * qh + 128 + 32 * g + 16);
+      bf16x8 ar;
+      if (ROPE) ar = *reinterpret_cast<const bf16x8*>(krow + kRopeOff + 64 * qh + 16 * g);
+      const i8v a0 = {(int)p00.x, (int)p00.y, (int)p00.z, (int)p00.w, (int)p01.x, (int)p01.y, (int)p01.z, (int)p01.w};
+      const i8v a1 = {(int)p10.x, (int)p10.y, (int)p10.z, (int)p10.w, (int)p11.x, (int)p11.y, (int)p11.z, (int)p11.w};
+      const f4 z4 = f4{0.0f, 0.0f, 0.0f, 0.0f};
+      f4 acc0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a0, qhi[0], z4, 0, 0, 0, 0, 0, 0);
+      f4 acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a1, qhi[1], z4, 0, 0, 0, 0, 0, 0);
+      f4 accr = z4;
+      if (ROPE) accr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar, qpe, z4, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a0, qlo[0], acc0, 0, 0, 0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a1, qlo[1], acc1, 0, 0, 0, 0, 0, 0);
       // chunk c + NST - 1 into the stage everyone finished before the barrier
       if (c + G::NST - 1 < nch) issue(nxt2, c + G::NST - 1);
       float pr[4];
@@ -410,11 +408,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
     float x[8];
     float nm = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float sc = *reinterpret_cast<const float*>(stg + key_row(2 * ps + (e >> 2), 4 * g + (e & 3)) * RB +
-                                                       kScaleOff + 4 * pt);
-      x[e] = p[e] * sc;             // padding rows: p = 0, sc finite (a copied row)
-      nm = fmaxf(nm, x[e]);
+    for (int bb = 0; bb < 2; ++bb) {
+      // slots 4bb..4bb+3 are four consecutive LDS rows
+      const uint8_t* srow = stg + key_row(2 * ps + bb, 4 * g) * RB + kScaleOff + 4 * pt;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float sc = *reinterpret_cast<const float*>(srow + r * RB);
+        x[4 * bb + r] = p[4 * bb + r] * sc;   // padding rows: p = 0, sc finite (a copied row)
+        nm = fmaxf(nm, x[4 * bb + r]);
+      }
     }
     nm = max_xg(nm);
     // power of two 2^ne >= nm; operands scaled into [0, 256].  oacc holds

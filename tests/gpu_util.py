@@ -13,7 +13,8 @@ from oracle import writer as oracle_writer
 DEV = "cuda:0"
 
 # Parity bar for attention outputs: max |o_gpu - o_ref| <= 2e-2 over all
-# elements, per-(row, head) relative L2 <= 1e-2, no NaN/Inf; lse within 1e-3.
+# elements, per-(row, head) relative L2 <= 1e-2, no NaN/Inf; lse within
+# 1e-3 * max(1, |lse|) (the LSE bar is this test suite's own addition).
 MAX_ABS = 2e-2
 MAX_REL_L2 = 1e-2
 MAX_LSE = 1e-3
@@ -103,5 +104,6 @@ def assert_parity(out: torch.Tensor, lse: torch.Tensor, ref_out, ref_lse, rows):
         inf = np.isneginf(rl)
         assert np.array_equal(np.isneginf(g), inf)
         assert np.all(np.isfinite(g[~inf]))
-        d = np.abs(g[~inf] - rl[~inf])
+        # relative for large scores: fp32 score accumulation carries ~1e-5 relative error
+        d = np.abs(g[~inf] - rl[~inf]) / np.maximum(1.0, np.abs(rl[~inf]))
         assert d.size == 0 or d.max() <= MAX_LSE, f"lse err {d.max():.3e}"

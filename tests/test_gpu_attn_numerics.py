@@ -1,0 +1,73 @@
+"""Numerical stress cases for the HIP attention: very peaked and very flat
+softmax, cache rows whose tile scales span many binades, all-zero rows, and
+top-k orders that make the running maximum move late or never."""
+import numpy as np
+import pytest
+
+import workloads as wl
+from oracle import attention as oracle_attn
+from tests.gpu_util import assert_parity, build_cache, oracle_cache, run_attn
+
+pytestmark = pytest.mark.gpu
+
+NUM_SLOTS = 8192
+
+
+def _cfg(seed, q_scale=1.0, row_scale_binades=0, zero_rows=0, rope_dim=64, T=8, W=1024):
+    rng = np.random.default_rng(seed)
+    n = NUM_SLOTS - 1
+    x = rng.standard_normal((n, 512), dtype=np.float32)
+    if row_scale_binades:
+        x *= np.exp2(rng.integers(-row_scale_binades, row_scale_binades + 1, size=(n, 1))).astype(np.float32)
+    if zero_rows:
+        x[rng.choice(n, size=zero_rows, replace=False)] = 0.0
+    latent = wl.bf16_bits_from_f32(x)
+    rope = wl.normal_bf16(rng, (n, rope_dim)) if rope_dim else None
+    q = wl.bf16_bits_from_f32(rng.standard_normal((T, 16, 512 + rope_dim), dtype=np.float32) * q_scale)
+    idx = wl.decode_topk(rng, T, W, NUM_SLOTS, 200, 4000, index_topk=W)
+    return dict(num_slots=NUM_SLOTS, rope_dim=rope_dim, T=T, H=16, W=W, latent=latent, rope=rope,
+                slots=np.arange(1, NUM_SLOTS, dtype=np.int64), q=q, idx=idx,
+                sm_scale=float(1.0 / np.sqrt(512 + rope_dim)), slot0=wl.slot0_bytes(rng, "ff"))
+
+
+def _check(cfg, idx=None):
+    cache = build_cache(cfg)
+    out, lse = run_attn(cfg, cache, idx=idx)
+    idx = cfg["idx"] if idx is None else idx
+    need = idx[idx >= 0]
+    ref = oracle_attn.sparse_mla_attn(cfg["q"], oracle_cache(cfg, need), idx, idx.shape[1],
+                                      cfg["rope_dim"], cfg["sm_scale"])
+    assert_parity(out, lse, ref[0], ref[1], range(cfg["T"]))
+    return ref
+
+
+@pytest.mark.parametrize("q_scale", [30.0, 0.01])
+def test_peaked_and_flat_softmax(q_scale):
+    print(f"q_scale={q_scale}", flush=True)
+    _check(_cfg(700, q_scale=q_scale))
+
+
+@pytest.mark.parametrize("rope_dim", [64, 0])
+def test_tile_scales_spanning_40_binades(rope_dim):
+    _check(_cfg(701, row_scale_binades=20, rope_dim=rope_dim))
+
+
+def test_all_zero_rows_mixed_in():
+    _check(_cfg(702, zero_rows=4000))
+
+
+@pytest.mark.parametrize("order", ["ascending", "descending"])
+def test_score_ordered_topk(order):
+    """Entries sorted by the oracle's score for head 0: the running maximum
+    then rises chunk after chunk, or is fixed by the first chunk."""
+    cfg = _cfg(703, q_scale=4.0)
+    cache = oracle_cache(cfg, cfg["idx"][cfg["idx"] >= 0])
+    idx = cfg["idx"].copy()
+    q = (cfg["q"].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    for t in range(cfg["T"]):
+        v = idx[t][idx[t] >= 0]
+        k = oracle_attn.dequant_rows(cache, v, cfg["rope_dim"])
+        s = k @ q[t, 0]
+        o = np.argsort(s if order == "ascending" else -s, kind="stable")
+        idx[t, : v.size] = v[o]
+    _check(cfg, idx=idx)
