@@ -9,8 +9,12 @@ pages, contexts U{1k..64k}.  `value` is algorithmic gathered KV bytes
 
 Caches are rotated across steps (several copies whose total exceeds the
 256 MB Infinity Cache), so each step's gathers come from HBM rather than a
-cache left warm by the previous step.  Per-kernel durations come from HIP
-events recorded on the stream the library launches on.
+cache left warm by the previous step.  The timed steps replay one HIP graph
+per cache copy (writer + attention, captured from the library's launches;
+the library allocates nothing, so the capture holds only the kernels), which
+keeps host launch overhead out of the step time; the first replay is checked
+bit for bit against an eager step.  Per-kernel durations come from HIP events
+recorded on the library's stream around bursts of back-to-back launches.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras]
 """
@@ -106,6 +110,23 @@ def main():
         n = max(2, int(np.ceil(600e6 / cache.numel())))   # > 2x the Infinity Cache
         return [cache] + [cache.clone() for _ in range(n - 1)]
 
+    def burst(launch, iters, warm):
+        """Average duration (us) of `iters` back-to-back launches between one
+        pair of events on the library's stream, after `warm` untimed ones."""
+        for i in range(warm):
+            launch(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        # a fixed-length GPU delay first, so that every launch of the burst is
+        # queued before the first one starts (host launch pacing stays out)
+        torch.cuda._sleep(int(2.0e6 + 150e3 * iters))
+        e0.record(stream)
+        for i in range(iters):
+            launch(warm + i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return np.array([e0.elapsed_time(e1) * 1e3 / iters])
+
     def time_attn(cfg, caches, iters, warm):
         q = bf16_dev(cfg["q"])
         idx = torch.from_numpy(cfg["idx"]).to(dev)
@@ -115,19 +136,10 @@ def main():
         lse = torch.empty((T, H), dtype=torch.float32, device=dev)
         ws_n = smla.workspace_size(T, H, W, cfg["rope_dim"])
         ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=dev)
-        evs = []
-        for i in range(warm + iters):
-            c = caches[i % len(caches)]
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            smla.attn(q, c, idx, cfg["sm_scale"], cfg["rope_dim"], topk_capacity=W,
-                      out=out, lse=lse, workspace=ws)
-            e1.record(stream)
-            if i >= warm:
-                evs.append((e0, e1))
-        torch.cuda.synchronize()
-        us = np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs])
-        return us, out, lse
+        def launch(i):
+            smla.attn(q, caches[i % len(caches)], idx, cfg["sm_scale"], cfg["rope_dim"],
+                      topk_capacity=W, out=out, lse=lse, workspace=ws)
+        return burst(launch, iters, warm), out, lse
 
     def gathered(cfg, row_bytes):
         idx = cfg["idx"]
@@ -151,31 +163,60 @@ def main():
     ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=dev)
     bytes_step = gathered(cfg, NOPE_ROW)
 
-    def step(i, ev=None):
+    def step(i):
         c = caches[i % len(caches)]
-        if ev is not None:
-            ev[0].record(stream)
         smla.kv_write(new_lat, None, new_slots, c)
-        if ev is not None:
-            ev[1].record(stream)
         smla.attn(q, c, idx, cfg["sm_scale"], 0, topk_capacity=W, out=out, lse=lse, workspace=ws)
-        if ev is not None:
-            ev[2].record(stream)
+
+    # one graph per cache copy; eager launches if capture is unavailable
+    launch_mode = "hip-graph"
+    graphs = []
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for k in range(len(caches)):
+                step(k)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        ref = out.clone()
+        for k in range(len(caches)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(k)
+            graphs.append(g)
+        out.zero_()
+        graphs[0].replay()
+        torch.cuda.synchronize()
+        if not torch.equal(out, ref):
+            raise RuntimeError("graph replay differs from the eager step")
+    except Exception as exc:   # noqa: BLE001 - report and fall back to eager launches
+        log(f"graph capture unavailable ({exc}); timing eager launches")
+        graphs, launch_mode = [], "eager"
+
+    def run_step(i):
+        if graphs:
+            graphs[i % len(graphs)].replay()
+        else:
+            step(i)
 
     for i in range(a.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(a.steps)]
-    log(f"timing {a.steps} steps")
+        run_step(i)
+    log(f"timing {a.steps} steps ({launch_mode})")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(a.steps):
-        step(a.warmup + i, evs[i])
+        run_step(a.warmup + i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / a.steps
-    attn_us = np.array([e[1].elapsed_time(e[2]) * 1e3 for e in evs])
-    wr_us = np.array([e[0].elapsed_time(e[1]) * 1e3 for e in evs])
+    del graphs
+    # per-kernel durations: bursts of back-to-back launches, caches rotated
+    attn_us = burst(lambda i: smla.attn(q, caches[i % len(caches)], idx, cfg["sm_scale"], 0,
+                                        topk_capacity=W, out=out, lse=lse, workspace=ws),
+                    a.steps, a.warmup)
+    wr_us = burst(lambda i: smla.kv_write(new_lat, None, new_slots, caches[i % len(caches)]),
+                  a.steps, a.warmup)
     value = bytes_step / (ms_per_step * 1e-3) / 1e9
     attn_gbs = bytes_step / (attn_us.mean() * 1e-6) / 1e9
     log(f"step {ms_per_step*1e3:.1f} us, attention {attn_us.mean():.1f} us "
@@ -201,6 +242,7 @@ def main():
                         "sparse_mla_attn",
             "batch": T, "heads": 16, "topk": 2048, "topk_width": W, "rope_dim": 0,
             "num_slots": cfg["num_slots"], "cache_rotation": len(caches),
+            "launch": launch_mode,
         },
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
         "attn_us": round(float(attn_us.mean()), 2),
@@ -236,16 +278,7 @@ def main():
             lat = bf16_dev(wc["latent"])
             rope = bf16_dev(wc["rope"]) if rope_dim else None
             sl = torch.from_numpy(wc["slots"]).to(dev)
-            us = []
-            for i in range(a.warmup + a.steps):
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                smla.kv_write(lat, rope, sl, cache)
-                e1.record(stream)
-                if i >= a.warmup:
-                    us.append((e0, e1))
-            torch.cuda.synchronize()
-            us = np.array([x.elapsed_time(y) * 1e3 for x, y in us])
+            us = burst(lambda i: smla.kv_write(lat, rope, sl, cache), a.steps, a.warmup)
             written = int((wc["slots"] > 0).sum())
             byts = written * ((1024 + (128 if rope_dim else 0)) + 656 + 8) + (8192 - written) * 8
             extras[f"writer_8192_rope{rope_dim}"] = {

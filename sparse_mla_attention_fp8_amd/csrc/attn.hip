@@ -6,34 +6,44 @@
 // top-k list (0 <= idx < num_slots).  Padding is never gathered and carries an
 // exact zero weight, so NaN-coded bytes in slot 0 cannot reach the output.
 //
-// Work decomposition.  One 256-thread workgroup (4 wavefronts) per
-// (split, query row, group of 16 heads).  A split owns a contiguous range of
-// the row's top-k buffer; the workgroup compacts the valid entries of its
+// Work decomposition.  One 512-thread workgroup (8 wavefronts, two per SIMD)
+// per (split, query row, group of 16 heads).  A split owns a contiguous range
+// of the row's top-k buffer; the workgroup compacts the valid entries of its
 // range into LDS and walks them in chunks of 64 keys:
 //
 //   gather  Each chunk's 64 rows (656 B, or the 528 B a NoPE reader needs)
 //           are copied HBM -> LDS with direct-to-LDS 16-byte loads, once per
-//           chunk and shared by all heads; a 3-stage ring keeps two chunks in
-//           flight while one is computed.  Entries past the valid count of the
-//           last chunk get a copy of the chunk's first valid row (so every LDS
-//           operand is finite) and a weight that is exactly zero by select.
-//   QK^T    Wavefront w scores keys 16w..16w+15 against all 16 heads:
-//           S^T = K Q^T on v_mfma_f32_16x16x32_fp8_fp8, fed directly with the
-//           cached e4m3 codes.  q (bf16) is split exactly into an e4m3 high
-//           part and an e4m3 residual after a power-of-two prescale, so two
-//           fp8 products give the bf16 q to within e4m3 subnormal flushing.
-//           Each 128-wide tile accumulates separately and is scaled by its
-//           fp32 tile scale; the RoPE part (bf16) uses the bf16 MFMA.
-//   softmax Base-2 online softmax: block maxima and sums cross the four
-//           wavefronts through LDS together with p * scale_tile.
-//   P.V     Wavefront w owns latent tile w (128 dims): O^T = V^T P^T with the
-//           e4m3 codes as V (transposed in registers from 8-byte LDS reads by
-//           byte permutes) and P * scale_tile split into e4m3 high + residual
-//           after a per-head power-of-two normalisation.
+//           chunk and shared by all heads, into a ring of 3 (RoPE) or 4
+//           (NoPE) stages.
+//           Entries past the valid count of the last chunk get a copy of the
+//           chunk's first valid row (so every LDS operand is finite) and a
+//           weight that is exactly zero.
+//   QK^T    Wavefront w scores the 16 keys of block w/2 against all 16 heads
+//           over latent half w%2 (two 128-dim tiles): S^T = K Q^T on
+//           v_mfma_scale_f32_16x16x128_f8f6f4 (unit scales), fed directly with
+//           the cached e4m3 codes.  q (bf16) is split into an e4m3 high part
+//           and an e4m3 residual after a power-of-two prescale, exact up to
+//           e4m3 subnormal flushing, so two fp8 products give the bf16 q.
+//           Each tile is scaled by its fp32 tile scale; the RoPE part (bf16)
+//           uses v_mfma_f32_16x16x32_bf16.  The two latent halves meet in LDS.
+//   softmax Base-2 online softmax, one state per (head, key half): wavefront w
+//           owns keys 32(w%2) .. 32(w%2)+31 of every chunk.  The running max is
+//           lazy (it moves only when a score passes it by 2^8).
+//   P.V     Wavefront w owns latent tile w/2 (128 dims) for its key half:
+//           O^T = V^T P^T on v_mfma_f32_16x16x32_fp8_fp8, V^T read from LDS
+//           with the 8-bit transpose read, P * scale_tile split into e4m3 high
+//           part + residual after a per-head power-of-two normaliser.
 //
-// With one split the workgroup writes the bf16 output and LSE; with several it
-// writes (O unnormalised fp32, m, l) partials that attn_merge combines.  m is
-// kept in log2 units throughout.
+// Software pipeline: iteration c scores chunk c+1 (QK^T, partial scores to
+// LDS) while it runs softmax and P.V on chunk c, whose V^T operands and tile
+// scales each P.V wavefront already holds in registers (read one iteration
+// earlier).  One workgroup barrier per chunk then both publishes the partial
+// scores and releases chunk c's stage, which is refilled at once, so three
+// chunks (NoPE) or two (RoPE) stay in flight while a chunk computes.
+//
+// The key halves merge through LDS at the end.  With one split the workgroup
+// writes the bf16 output and LSE; with several it writes (O unnormalised fp32,
+// m, l) partials that attn_merge combines.  m is kept in log2 units throughout.
 #include "common.h"
 
 namespace smla {
@@ -146,13 +156,20 @@ __device__ __forceinline__ void tr4x4(uint32_t a0, uint32_t a1, uint32_t a2, uin
   b3 = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
 }
 
+// Max without NaN canonicalisation (operands are never signalling NaNs).
+__device__ __forceinline__ float fmax_nc(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // Reductions over the four lanes l, l^16, l^32, l^48 that hold one head (VALU
 // row swaps; no LDS round trip).
 __device__ __forceinline__ float max_xg(float v) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  v = fmax_nc(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return fmax_nc(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float sum_xg(float v) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -214,7 +231,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
 
   __shared__ __align__(16) uint8_t stages[G::NST * G::STAGE];   // ring of 64-row stages
   __shared__ int slot_list[kMaxRange];
-  __shared__ __align__(16) float4 xs[4][2][64];   // [block][dim half][lane]: partial scores, keys 4g+r
+  __shared__ __align__(16) float4 xs[2][4][2][64];   // [chunk & 1][block][dim half][lane]: partial scores, keys 4g+r
   __shared__ int wave_counts[kWaves];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -275,7 +292,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
     qe = qe > 126 ? 126 : (qe < -126 ? -126 : qe);
   }
   const float qscale = exp2_pow(qe);
-  const float qinv = exp2_pow(-qe);
+  // latent score = qs * sum_tiles scale_tile * <code, q_hi + q_lo>, already in log2 units
+  const float qs = exp2_pow(-qe) * sm_scale_log2;
   i8v qhi[2], qlo[2];   // B operands of v_mfma_f32_16x16x128_f8f6f4, one per tile
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
@@ -328,140 +346,86 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
     }
   };
 
-  float m_run = -INFINITY;   // running max (log2 units) of this key half, per head
+  // running max (log2 units) of this key half, per head; a finite sentinel
+  // until the first valid key, so that exp2(-inf - m_run) is an exact 0
+  float m_run = -1e30f;
   float l_run = 0.0f;        // running sum over this lane's keys (4g + r)
   int ne_run = 8;            // oacc = O * 2^(8 - ne_run)
   int ne_hi = -126;
+  float x_lim = 256.0f;      // 2^ne_run: largest P * scale the normaliser takes
+  float inv_run = 1.0f;      // 2^(8 - ne_run)
   f4 oacc[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) oacc[c] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  auto compute = [&](const uint8_t* stg, int c, uint32_t nxt2) {
-    const int nv = min(kKeys, n - c * kKeys);
-    // ---------------- QK^T partial: keys 16qb + [0,16), dims half qh ----------------
-    {
-      const uint8_t* krow = stg + key_row(qb, n16) * RB;
-      const uint4 p00 = *reinterpret_cast<const uint4*>(krow + 256 * qh + 32 * g);
-      const uint4 p01 = *reinterpret_cast<const uint4*>(krow + 256 * qh + 32 * g + 16);
-      const uint4 p10 = *reinterpret_cast<const uint4*>(krow + 256 * qh + 128 + 32 * g);
-      const uint4 p11 = *reinterpret_cast<const uint4*>(krow + 256 * qh + 128 + 32 * g + 16);
-      bf16x8 ar;
-      if (ROPE) ar = *reinterpret_cast<const bf16x8*>(krow + kRopeOff + 64 * qh + 16 * g);
-      const i8v a0 = {(int)p00.x, (int)p00.y, (int)p00.z, (int)p00.w, (int)p01.x, (int)p01.y, (int)p01.z, (int)p01.w};
-      const i8v a1 = {(int)p10.x, (int)p10.y, (int)p10.z, (int)p10.w, (int)p11.x, (int)p11.y, (int)p11.z, (int)p11.w};
-      const f4 z4 = f4{0.0f, 0.0f, 0.0f, 0.0f};
-      f4 acc0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a0, qhi[0], z4, 0, 0, 0, 0, 0, 0);
-      f4 acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a1, qhi[1], z4, 0, 0, 0, 0, 0, 0);
-      f4 accr = z4;
-      if (ROPE) accr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar, qpe, z4, 0, 0, 0);
-      acc0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a0, qlo[0], acc0, 0, 0, 0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a1, qlo[1], acc1, 0, 0, 0, 0, 0, 0);
-      // chunk c + NST - 1 into the stage everyone finished before the barrier
-      if (c + G::NST - 1 < nch) issue(nxt2, c + G::NST - 1);
-      float pr[4];
+  const int k8 = n16 >> 1, h8 = n16 & 1;
+  // P.V operands of a chunk, read from its stage one iteration ahead: V^T of
+  // tile pt for keys 32ps + [0, 32) through the LDS transpose read (within each
+  // 16-lane group, source lane 2k+h reads 8 bytes of slot k's row at dims
+  // d0 + 8h; lane i then holds dim d0 + i of the group's 8 slots, byte k =
+  // slot k), and the tile-pt scales of this lane's 8 keys (4g + r of blocks
+  // 2ps and 2ps + 1).
+  long va[8];
+  float sc[8];
+  auto read_pv = [&](const uint8_t* stg, long* v, float* s) {
+    const uint8_t* vsrc = stg + key_row(2 * ps + (k8 >> 2), 4 * g + (k8 & 3)) * RB + 128 * pt + 8 * h8;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float2 sc = *reinterpret_cast<const float2*>(stg + key_row(qb, 4 * g + r) * RB +
-                                                           kScaleOff + 8 * qh);
-        pr[r] = qinv * (sc.x * acc0[r] + sc.y * acc1[r]) + accr[r];
-      }
-      xs[qb][qh][lane] = make_float4(pr[0], pr[1], pr[2], pr[3]);
+    for (int cc = 0; cc < 8; ++cc) {
+      const v2i tv = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(vsrc + 16 * cc));
+      v[cc] = pack64((uint32_t)tv[0], (uint32_t)tv[1]);
     }
-    lds_barrier();
-
-    // ---------------- softmax over keys 32ps + [0,32) ----------------
-    if (nv <= 32 * ps) return;          // no valid key in this half of the chunk
-    float sv[8];
-#pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
-      const float4 u0 = xs[2 * ps + bb][0][lane];
-      const float4 u1 = xs[2 * ps + bb][1][lane];
-      sv[4 * bb + 0] = (u0.x + u1.x) * sm_scale_log2;
-      sv[4 * bb + 1] = (u0.y + u1.y) * sm_scale_log2;
-      sv[4 * bb + 2] = (u0.z + u1.z) * sm_scale_log2;
-      sv[4 * bb + 3] = (u0.w + u1.w) * sm_scale_log2;
-    }
-    if (nv < kKeys) {                   // last chunk: padding rows score -inf
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (key_row(2 * ps + (e >> 2), 4 * g + (e & 3)) >= nv) sv[e] = -INFINITY;
-    }
-    float mloc = sv[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) mloc = fmaxf(mloc, sv[e]);
-    mloc = max_xg(mloc);                // finite: row 32ps is valid
-    // Lazy running max: it moves only when a score exceeds it by more than
-    // 2^8, so p <= 256 and most chunks leave O's scale untouched.
-    const float m_new = mloc > m_run + 8.0f ? mloc : m_run;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 1 unless m moved
-    float p[8];
-    float psum = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      p[e] = __builtin_amdgcn_exp2f(sv[e] - m_new);   // -inf -> exactly 0
-      psum += p[e];
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-
-    // ---------------- P.V for tile pt ----------------
-    float x[8];
-    float nm = 0.0f;
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
       // slots 4bb..4bb+3 are four consecutive LDS rows
       const uint8_t* srow = stg + key_row(2 * ps + bb, 4 * g) * RB + kScaleOff + 4 * pt;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float sc = *reinterpret_cast<const float*>(srow + r * RB);
-        x[4 * bb + r] = p[4 * bb + r] * sc;   // padding rows: p = 0, sc finite (a copied row)
-        nm = fmaxf(nm, x[4 * bb + r]);
-      }
-    }
-    nm = max_xg(nm);
-    // power of two 2^ne >= nm; operands scaled into [0, 256].  oacc holds
-    // O * 2^(8 - ne_run); the normaliser follows each chunk but stays within
-    // 2^96 of the largest one seen, which bounds oacc by 2^(11+9+8+96) < 2^128.
-    int ne = 0;
-    if (nm > 0.0f) {
-      const uint32_t bits = __float_as_uint(nm);
-      ne = (int)((bits >> 23) & 0xFF) - 127 + ((bits & 0x7FFFFF) ? 1 : 0);
-      ne = ne > 119 ? 119 : (ne < -118 ? -118 : ne);
-    }
-    ne_hi = ne > ne_hi ? ne : ne_hi;
-    ne = ne < ne_hi - 96 ? ne_hi - 96 : ne;
-    // keep the previous normaliser unless the chunk would exceed 256 or sit
-    // more than 8 binades below it
-    if (ne <= ne_run && ne >= ne_run - 8) ne = ne_run;
-    const float inv = exp2_pow(8 - ne);
-    const float resc = ldexpf(alpha, ne_run - ne);
-    ne_run = ne;
-    if (!__all(resc == 1.0f)) {
-#pragma unroll
-      for (int cc = 0; cc < 8; ++cc)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) oacc[cc][r] *= resc;
-    }
-    uint32_t h0, l0, h1, l1;
-    split_e4m3(x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv, h0, l0);
-    split_e4m3(x[4] * inv, x[5] * inv, x[6] * inv, x[7] * inv, h1, l1);
-    const long bhi = pack64(h0, h1), blo = pack64(l0, l1);
-    // V^T through the LDS transpose read: within each 16-lane group, source
-    // lane 2k+h reads 8 bytes of slot k's row at dims d0 + 8h; lane i then holds
-    // dim d0 + i of the group's 8 slots (byte k = slot k), the A operand of
-    // one 16-dim block.
-    const int k8 = n16 >> 1, h8 = n16 & 1;
-    const uint8_t* vsrc = stg + key_row(2 * ps + (k8 >> 2), 4 * g + (k8 & 3)) * RB + 128 * pt + 8 * h8;
-#pragma unroll
-    for (int cc = 0; cc < 8; ++cc) {
-      const v2i tv = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(vsrc + 16 * cc));
-      const long a = pack64((uint32_t)tv[0], (uint32_t)tv[1]);
-      oacc[cc] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, bhi, oacc[cc], 0, 0, 0);
-      oacc[cc] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, blo, oacc[cc], 0, 0, 0);
+      for (int r = 0; r < 4; ++r) s[4 * bb + r] = *reinterpret_cast<const float*>(srow + r * RB);
     }
   };
+  // QK^T partial of a chunk: keys 16qb + [0,16), dims half qh.  The products
+  // are issued early and combined late, so nothing waits on them in between.
+  struct QkLoad { i8v a0, a1; bf16x8 ar; float2 sq[4]; };
+  struct QkPart { f4 acc0, acc1, accr; float2 sq[4]; };
+  auto qk_load = [&](const uint8_t* stg) {
+    QkLoad o;
+    const uint8_t* krow = stg + key_row(qb, n16) * RB;
+    const uint4 p00 = *reinterpret_cast<const uint4*>(krow + 256 * qh + 32 * g);
+    const uint4 p01 = *reinterpret_cast<const uint4*>(krow + 256 * qh + 32 * g + 16);
+    const uint4 p10 = *reinterpret_cast<const uint4*>(krow + 256 * qh + 128 + 32 * g);
+    const uint4 p11 = *reinterpret_cast<const uint4*>(krow + 256 * qh + 128 + 32 * g + 16);
+    if (ROPE) o.ar = *reinterpret_cast<const bf16x8*>(krow + kRopeOff + 64 * qh + 16 * g);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      o.sq[r] = *reinterpret_cast<const float2*>(stg + key_row(qb, 4 * g + r) * RB + kScaleOff + 8 * qh);
+    o.a0 = i8v{(int)p00.x, (int)p00.y, (int)p00.z, (int)p00.w, (int)p01.x, (int)p01.y, (int)p01.z, (int)p01.w};
+    o.a1 = i8v{(int)p10.x, (int)p10.y, (int)p10.z, (int)p10.w, (int)p11.x, (int)p11.y, (int)p11.z, (int)p11.w};
+    return o;
+  };
+  auto qk_mfma = [&](const QkLoad& k) {
+    QkPart o;
+    const f4 z4 = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    o.acc0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k.a0, qhi[0], z4, 0, 0, 0, 0, 0, 0);
+    o.acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k.a1, qhi[1], z4, 0, 0, 0, 0, 0, 0);
+    o.accr = z4;
+    if (ROPE) o.accr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k.ar, qpe, z4, 0, 0, 0);
+    o.acc0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k.a0, qlo[0], o.acc0, 0, 0, 0, 0, 0, 0);
+    o.acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k.a1, qlo[1], o.acc1, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o.sq[r] = k.sq[r];
+    return o;
+  };
+  // partial scores (log2 units) of MFMA rows 4g + r, head n16 -> xs[c & 1]
+  auto qk_finish = [&](const QkPart& o, int c) {
+    float pr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float lat = o.sq[r].x * o.acc0[r] + o.sq[r].y * o.acc1[r];
+      pr[r] = ROPE ? lat * qs + o.accr[r] * sm_scale_log2 : lat * qs;
+    }
+    xs[c & 1][qb][qh][lane] = make_float4(pr[0], pr[1], pr[2], pr[3]);
+  };
 
-  // ---- pipeline: chunk c lives in stage c % NST; NST - 1 chunks in flight ----
+  // ---- pipeline: chunk c lives in stage c % NST ----
   const uint32_t lds0 = lds_addr(stages);
   // Every compiler-visible load (q) is complete before the pipeline starts, so
   // the compiler has no reason to emit a vmcnt wait of its own in the loop
@@ -469,22 +433,140 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
   // drain the whole pipeline).
   __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
-  for (int c = 0; c < G::NST - 1; ++c)
+  for (int c = 0; c < G::NST; ++c)
     if (c < nch) issue(lds0 + (uint32_t)(c * G::STAGE), c);
-  int cur = 0;                       // stage of chunk c
+  // chunk 0: wait for it (chunks 1 .. NST-1 stay in flight), score it, read its P.V operands
+  if (nch > 0) {
+    const int ahead = min(G::NST - 1, nch - 1);
+    if (ahead <= 0) vm_barrier<0>();
+    else if (ahead == 1) { if (big) vm_barrier<CNT0>(); else vm_barrier<CNT1>(); }
+    else if (ahead == 2) { if (big) vm_barrier<2 * CNT0>(); else vm_barrier<2 * CNT1>(); }
+    else { if (big) vm_barrier<3 * CNT0>(); else vm_barrier<3 * CNT1>(); }
+    qk_finish(qk_mfma(qk_load(stages)), 0);
+    read_pv(stages, va, sc);
+  }
   for (int c = 0; c < nch; ++c) {
-    // this wave's gathers issued after chunk c's: those of chunks c+1 .. c+NST-2
-    const int ahead = min(G::NST - 2, nch - 1 - c);
-    if (ahead <= 0) {
-      vm_barrier<0>();
-    } else if (ahead == 1) {
-      if (big) vm_barrier<CNT0>(); else vm_barrier<CNT1>();
-    } else {
-      if (big) vm_barrier<2 * CNT0>(); else vm_barrier<2 * CNT1>();
+    // Chunk c+1 landed (this wave's loads issued after it: chunks c+2 ..
+    // c+NST-1 that exist), and after the barrier chunk c's partial scores are
+    // visible and nobody reads chunk c's stage any more.
+    const int ahead = min(G::NST - 2, nch - 2 - c);
+    if (ahead <= 0) vm_barrier<0>();
+    else if (ahead == 1) { if (big) vm_barrier<CNT0>(); else vm_barrier<CNT1>(); }
+    else { if (big) vm_barrier<2 * CNT0>(); else vm_barrier<2 * CNT1>(); }
+    const int cur = c % G::NST;
+    if (c + G::NST < nch) issue(lds0 + (uint32_t)(cur * G::STAGE), c + G::NST);
+
+    // Chunk c's partial scores are read first: LDS reads return in order, so
+    // the softmax then waits only for these, not for chunk c+1's operands.
+    float4 u[2][2];
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) u[bb][h] = xs[c & 1][2 * ps + bb][h][lane];
+
+    // ---- next chunk's operands (for the last chunk: stale bytes, results unused) ----
+    const uint8_t* nstg = stages + ((c + 1) % G::NST) * G::STAGE;
+    const QkLoad nk = qk_load(nstg);
+    long va_n[8];
+    float sc_n[8];
+    read_pv(nstg, va_n, sc_n);
+
+    // ---------------- softmax over keys 32ps + [0,32) of chunk c ----------------
+    // An empty key half (last chunk) scores -inf throughout and adds exact zeros.
+    const int nv = min(kKeys, n - c * kKeys);
+    float sv[8];
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      sv[4 * bb + 0] = u[bb][0].x + u[bb][1].x;
+      sv[4 * bb + 1] = u[bb][0].y + u[bb][1].y;
+      sv[4 * bb + 2] = u[bb][0].z + u[bb][1].z;
+      sv[4 * bb + 3] = u[bb][0].w + u[bb][1].w;
     }
-    const int nxt = cur == 0 ? G::NST - 1 : cur - 1;   // stage of chunk c + NST - 1
-    compute(stages + cur * G::STAGE, c, lds0 + (uint32_t)(nxt * G::STAGE));
-    cur = cur == G::NST - 1 ? 0 : cur + 1;
+    if (nv < kKeys) {                   // last chunk: padding rows score -inf
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (key_row(2 * ps + (e >> 2), 4 * g + (e & 3)) >= nv) sv[e] = -INFINITY;
+    }
+    // Lazy running max: it moves only when a score exceeds it by more than
+    // 2^8, so p <= 256 and most chunks leave O's scale untouched.  Whether any
+    // head moves is a per-lane test and a wave vote; only then does the
+    // wavefront reduce across lanes.
+    float lmax = sv[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) lmax = fmaxf(lmax, sv[e]);
+    const bool moved = __any(lmax > m_run + 8.0f);   // true on the first chunk with a valid key
+    float alpha = 1.0f;
+    if (moved) {
+      const float mloc = max_xg(lmax);
+      const float m_new = mloc > m_run + 8.0f ? mloc : m_run;
+      alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 1 unless this head's max moved
+      m_run = m_new;
+    }
+    float p[8];
+    float psum = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      p[e] = __builtin_amdgcn_exp2f(sv[e] - m_run);   // -inf -> exactly 0
+      psum += p[e];
+    }
+    l_run = l_run * alpha + psum;
+
+    // ---------------- P.V for tile pt ----------------
+    float x[8];
+    float xmax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x[e] = p[e] * sc[e];              // padding rows: p = 0, sc finite (a copied row)
+      xmax = fmaxf(xmax, x[e]);
+    }
+    // The normaliser 2^ne (oacc holds O * 2^(8 - ne_run), operands scaled into
+    // [0, 256]) changes only when the max moved or a product outgrows it;
+    // otherwise it is kept, which needs no cross-lane work.  It is set from the
+    // largest product since the max last moved (within 2^1), so e4m3 flushing
+    // drops only terms below 2^-17 of the largest one.
+    if (moved || __any(xmax > x_lim)) {
+      const float nm = max_xg(xmax);
+      int ne = 0;
+      if (nm > 0.0f) {
+        const uint32_t bits = __float_as_uint(nm);
+        ne = (int)((bits >> 23) & 0xFF) - 127 + ((bits & 0x7FFFFF) ? 1 : 0);
+        ne = ne > 119 ? 119 : (ne < -118 ? -118 : ne);
+      }
+      // the normaliser stays within 2^96 of the largest one seen, which
+      // bounds oacc by 2^(11+9+8+96) < 2^128
+      ne_hi = ne > ne_hi ? ne : ne_hi;
+      ne = ne < ne_hi - 96 ? ne_hi - 96 : ne;
+      // a head whose max did not move keeps a normaliser that still fits
+      if (alpha == 1.0f && ne <= ne_run) ne = ne_run;
+      const float resc = ldexpf(alpha, ne_run - ne);
+      ne_run = ne;
+      x_lim = exp2_pow(ne);
+      inv_run = exp2_pow(8 - ne);
+      if (!__all(resc == 1.0f)) {
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) oacc[cc][r] *= resc;
+      }
+    }
+    const float inv = inv_run;
+    uint32_t h0, l0, h1, l1;
+    split_e4m3(x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv, h0, l0);
+    split_e4m3(x[4] * inv, x[5] * inv, x[6] * inv, x[7] * inv, h1, l1);
+    const long bhi = pack64(h0, h1), blo = pack64(l0, l1);
+    // next chunk's QK^T products, then this chunk's P.V, then the next scores
+    const QkPart nq = qk_mfma(nk);
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc)
+      oacc[cc] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(va[cc], bhi, oacc[cc], 0, 0, 0);
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc)
+      oacc[cc] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(va[cc], blo, oacc[cc], 0, 0, 0);
+    if (c + 1 < nch) qk_finish(nq, c + 1);
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) va[cc] = va_n[cc];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sc[e] = sc_n[e];
   }
 
   // ---- combine the two key halves, then write ------------------------------
@@ -508,8 +590,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
   if (ps == 1 || !hvalid) return;
   const float2 o1 = ml[slot4];
   const float M = fmaxf(m_run, o1.x);
-  const float w0 = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - M);
-  const float w1 = o1.x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(o1.x - M);
+  // (a half without valid keys has l = 0, so its weight does not matter)
+  const float w0 = __builtin_amdgcn_exp2f(m_run - M);
+  const float w1 = __builtin_amdgcn_exp2f(o1.x - M);
   const float L = w0 * l_full + w1 * o1.y;
   // oacc[c][r] (and mo) hold dim 128pt + 16c + 4g + r
   const int dim0 = 128 * pt + 4 * g;

@@ -86,13 +86,21 @@ def oracle_for(cfg: dict, rows, idx: np.ndarray | None = None, W: int | None = N
                                        rows=list(rows))
 
 
-def assert_parity(out: torch.Tensor, lse: torch.Tensor, ref_out, ref_lse, rows):
+def assert_parity(out: torch.Tensor, lse: torch.Tensor, ref_out, ref_lse, rows, abs_bound=None,
+                  unit_scale=True):
+    """The parity bar on the listed query rows.  `abs_bound` (same shape as the
+    selected outputs) adds an elementwise error bound; `unit_scale=False` drops
+    the absolute 2e-2 bar, which is only meaningful for unit-scale data."""
     rows = np.asarray(rows)
     o = to_f64(out)[rows]
     r = ref_out[rows]
     assert np.all(np.isfinite(o)), "non-finite attention output"
     err = np.abs(o - r)
-    assert err.max() <= MAX_ABS, f"max abs err {err.max():.3e}"
+    if unit_scale:
+        assert err.max() <= MAX_ABS, f"max abs err {err.max():.3e}"
+    if abs_bound is not None:
+        excess = err / abs_bound
+        assert excess.max() <= 1.0, f"error exceeds the arithmetic bound by {excess.max():.3f}x"
     num = np.sqrt(((o - r) ** 2).sum(axis=-1))
     den = np.maximum(np.sqrt((r ** 2).sum(axis=-1)), 1e-30)
     empty = np.sqrt((r ** 2).sum(axis=-1)) == 0

@@ -1,6 +1,18 @@
 """Numerical stress cases for the HIP attention: very peaked and very flat
 softmax, cache rows whose tile scales span many binades, all-zero rows, and
-top-k orders that make the running maximum move late or never."""
+top-k orders that make the running maximum move late or never.
+
+Besides the standard bar (where the data is unit scale) every output element
+is held to the bound that the kernel's arithmetic implies, at any scale.  With
+w_k the exact softmax weights and v_k the dequantised value rows:
+  * each weighted scale p_k * s_k enters the e4m3 P.V product as a high part
+    plus an e4m3 residual: relative error <= 2^-8 per term;
+  * e4m3 flushing in that split drops, per term, less than 2^-17 of the
+    largest weighted scale max_j p_j s_j; times a code (|c| <= 448) that is at
+    most 2^-17 max_j w_j amax_j, amax_j the tile's largest |v|;
+  * the output is rounded to bf16: 2^-9 relative;
+  * scores and sums accumulate in fp32 (covered by the factor 2 of slack).
+So |o - o_ref| <= 2^-7 sum_k w_k |v_k| + 2^-16 n max_k w_k amax_k + 2^-8 |o_ref|."""
 import numpy as np
 import pytest
 
@@ -30,14 +42,33 @@ def _cfg(seed, q_scale=1.0, row_scale_binades=0, zero_rows=0, rope_dim=64, T=8, 
                 sm_scale=float(1.0 / np.sqrt(512 + rope_dim)), slot0=wl.slot0_bytes(rng, "ff"))
 
 
-def _check(cfg, idx=None):
+def _bound(cfg, host_cache, idx, ref_out):
+    """Elementwise error bound (module docstring) for every (row, head, dim)."""
+    q = (cfg["q"].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    bound = np.empty_like(ref_out)
+    for t in range(cfg["T"]):
+        v = oracle_attn.valid_entries(idx[t], idx.shape[1], cfg["num_slots"])
+        k = oracle_attn.dequant_rows(host_cache, v, cfg["rope_dim"])
+        s = cfg["sm_scale"] * (q[t] @ k.T)                    # [H][n]
+        w = np.exp(s - s.max(axis=1, keepdims=True))
+        w /= w.sum(axis=1, keepdims=True)
+        va = np.abs(k[:, :512])
+        amax = va.reshape(-1, 4, 128).max(axis=2)              # [n][tile]
+        wmax = np.repeat((w[:, :, None] * amax[None]).max(axis=1), 128, axis=1)   # [H][512]
+        bound[t] = 2.0**-7 * (w @ va) + 2.0**-16 * v.size * wmax + 2.0**-8 * np.abs(ref_out[t])
+    return bound + 1e-30
+
+
+def _check(cfg, idx=None, unit_scale=True):
     cache = build_cache(cfg)
     out, lse = run_attn(cfg, cache, idx=idx)
     idx = cfg["idx"] if idx is None else idx
     need = idx[idx >= 0]
-    ref = oracle_attn.sparse_mla_attn(cfg["q"], oracle_cache(cfg, need), idx, idx.shape[1],
+    host_cache = oracle_cache(cfg, need)
+    ref = oracle_attn.sparse_mla_attn(cfg["q"], host_cache, idx, idx.shape[1],
                                       cfg["rope_dim"], cfg["sm_scale"])
-    assert_parity(out, lse, ref[0], ref[1], range(cfg["T"]))
+    assert_parity(out, lse, ref[0], ref[1], range(cfg["T"]),
+                  abs_bound=_bound(cfg, host_cache, idx, ref[0]), unit_scale=unit_scale)
     return ref
 
 
@@ -49,7 +80,7 @@ def test_peaked_and_flat_softmax(q_scale):
 
 @pytest.mark.parametrize("rope_dim", [64, 0])
 def test_tile_scales_spanning_40_binades(rope_dim):
-    _check(_cfg(701, row_scale_binades=20, rope_dim=rope_dim))
+    _check(_cfg(701, row_scale_binades=20, rope_dim=rope_dim), unit_scale=False)
 
 
 def test_all_zero_rows_mixed_in():
