@@ -14,7 +14,9 @@
 //   gather  Each chunk's 64 rows (656 B, or the 528 B a NoPE reader needs)
 //           are copied HBM -> LDS with direct-to-LDS 16-byte loads, once per
 //           chunk and shared by all heads, into a ring of 3 (RoPE) or 4
-//           (NoPE) stages.
+//           (NoPE) stages.  Below 4 GiB of cache the loads take a scalar
+//           base and a 32-bit per-lane offset (one 24-bit multiply-add per
+//           load); larger caches use 64-bit per-lane addresses.
 //           Entries past the valid count of the last chunk get a copy of the
 //           chunk's first valid row (so every LDS operand is finite) and a
 //           weight that is exactly zero.
@@ -98,6 +100,21 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+      : "memory");
+}
+
+// The same load with a scalar 64-bit base and a 32-bit per-lane byte offset
+// (caches below 4 GiB): the address needs no 64-bit arithmetic per lane.
+__device__ __forceinline__ void dma16_sbase(const uint8_t* base, uint32_t off, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds_base))
       : "memory");
 }
 
@@ -220,7 +237,8 @@ __device__ int compact_valid(const int32_t* __restrict__ idx, int lo, int hi, in
   return total;
 }
 
-template <int ROPE>
+// SMALL: the cache spans less than 4 GiB, so row byte offsets fit 32 bits.
+template <int ROPE, bool SMALL>
 __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ cache, int64_t num_slots,
     const int32_t* __restrict__ idx, int64_t idx_stride, int W, int H, float sm_scale_log2,
@@ -335,13 +353,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
     // all slot lookups first (rows past the valid count take the chunk's first
     // row), so the loads below do not each wait on an LDS round trip
     int slot[CNT0];
+    if (nv == kKeys) {
 #pragma unroll
-    for (int j = 0; j < CNT0; ++j) slot[j] = slot_list[base + (seg_row[j] < nv ? seg_row[j] : 0)];
+      for (int j = 0; j < CNT0; ++j) slot[j] = slot_list[base + seg_row[j]];
+    } else {
+#pragma unroll
+      for (int j = 0; j < CNT0; ++j) slot[j] = slot_list[base + (seg_row[j] < nv ? seg_row[j] : 0)];
+    }
 #pragma unroll
     for (int j = 0; j < CNT0; ++j) {
       if (j < my_cnt) {
-        const uint8_t* src = cache + (int64_t)slot[j] * kRowBytes + seg_off[j];
-        dma16(src, stage + 1024u * (uint32_t)(wave + kWaves * j));
+        const uint32_t lds = stage + 1024u * (uint32_t)(wave + kWaves * j);
+        if (SMALL) {
+          dma16_sbase(cache, __umul24((uint32_t)slot[j], (uint32_t)kRowBytes) + (uint32_t)seg_off[j], lds);
+        } else {
+          dma16(cache + (int64_t)slot[j] * kRowBytes + seg_off[j], lds);
+        }
       }
     }
   };
@@ -702,14 +729,18 @@ hipError_t launch_attn(const uint16_t* q, const uint8_t* cache, int64_t num_slot
   }
   const int64_t blocks = (int64_t)plan.splits * T * plan.head_groups;
   const float sl2 = sm_scale * kLog2e;
-  if (rope_dim == 64)
-    hipLaunchKernelGGL(attn_mfma_kernel<64>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, q,
-                       cache, num_slots, idx, idx_stride, W, H, sl2, plan.range, plan.splits,
-                       plan.head_groups, out, lse, part_o, part_ml);
-  else
-    hipLaunchKernelGGL(attn_mfma_kernel<0>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, q,
-                       cache, num_slots, idx, idx_stride, W, H, sl2, plan.range, plan.splits,
-                       plan.head_groups, out, lse, part_o, part_ml);
+  // row byte offsets fit 32 bits (and slot * 656 fits the 24-bit multiply)
+  const bool small = num_slots <= (int64_t)(0xFFFFFFFFull / kRowBytes) && num_slots < (1 << 24);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, q, cache, num_slots,
+                       idx, idx_stride, W, H, sl2, plan.range, plan.splits, plan.head_groups, out,
+                       lse, part_o, part_ml);
+  };
+  if (rope_dim == 64) {
+    if (small) go(attn_mfma_kernel<64, true>); else go(attn_mfma_kernel<64, false>);
+  } else {
+    if (small) go(attn_mfma_kernel<0, true>); else go(attn_mfma_kernel<0, false>);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.splits == 1) return e;
   hipLaunchKernelGGL(attn_merge_kernel, dim3(T * H), dim3(64), 0, stream, part_o, part_ml,

@@ -8,6 +8,7 @@ import pytest
 import torch
 
 import workloads as wl
+import sparse_mla_attention_fp8_amd as smla
 from tests.gpu_util import (DEV, assert_parity, build_cache, oracle_for, run_attn, to_f64)
 
 pytestmark = pytest.mark.gpu
@@ -180,3 +181,45 @@ def test_deterministic():
     a = run_attn(cfg, cache)
     b = run_attn(cfg, cache)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("rope_dim", [0, 64])
+def test_cache_beyond_4_gib(rope_dim):
+    """A cache of 7,000,000 slots (4.6 GB): row byte offsets past 2^32 take the
+    kernel's 64-bit address path.  Only the referenced rows are written (on the
+    GPU by the writer, and in the oracle's lazily zeroed host copy)."""
+    from oracle import attention as oracle_attn
+    from oracle import writer as oracle_writer
+    print(f"cache beyond 4 GiB rope={rope_dim}", flush=True)
+    num_slots = 7_000_000
+    assert num_slots * wl.ROW_BYTES > 2**32
+    rng = np.random.default_rng(600 + rope_dim)
+    T, H, W = 4, 16, 384
+    idx = np.full((T, W), -1, dtype=np.int32)
+    for t in range(T):
+        n = 200 + 40 * t
+        hi = rng.choice(np.arange(6_600_000, num_slots), size=n // 2, replace=False)   # beyond 4 GiB
+        lo = rng.choice(np.arange(1, 6_500_000), size=n - n // 2, replace=False)
+        v = np.concatenate([hi, lo])
+        rng.shuffle(v)
+        idx[t, :n] = v
+    slots = np.unique(idx[idx >= 0]).astype(np.int64)
+    latent = wl.normal_bf16(rng, (slots.size, 512))
+    rope = wl.normal_bf16(rng, (slots.size, rope_dim)) if rope_dim else None
+    cache = torch.empty((num_slots, wl.ROW_BYTES), dtype=torch.uint8, device=DEV)
+    cache[0] = 0x7F
+    lat_d = torch.from_numpy(latent.view(np.int16)).view(torch.bfloat16).to(DEV)
+    rope_d = torch.from_numpy(rope.view(np.int16)).view(torch.bfloat16).to(DEV) if rope_dim else None
+    smla.kv_write(lat_d, rope_d, torch.from_numpy(slots).to(DEV), cache)
+    q = wl.normal_bf16(rng, (T, H, 512 + rope_dim))
+    sm = float(1.0 / np.sqrt(512 + rope_dim))
+    out, lse = smla.attn(torch.from_numpy(q.view(np.int16)).view(torch.bfloat16).to(DEV), cache,
+                         torch.from_numpy(idx).to(DEV), sm, rope_dim)
+    torch.cuda.synchronize()
+    host = np.zeros((num_slots, wl.ROW_BYTES), dtype=np.uint8)       # untouched pages stay unallocated
+    host[slots] = oracle_writer.encode_rows(latent, rope)
+    host[0] = 0x7F
+    assert np.array_equal(cache[torch.from_numpy(slots).to(DEV)].cpu().numpy(), host[slots])
+    ref_out, ref_lse = oracle_attn.sparse_mla_attn(q, host, idx, W, rope_dim, sm)
+    del cache
+    assert_parity(out, lse, ref_out, ref_lse, range(T))
