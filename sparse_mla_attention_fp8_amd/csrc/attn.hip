@@ -180,6 +180,15 @@ __device__ __forceinline__ float fmax_nc(float a, float b) {
   return r;
 }
 
+__device__ __forceinline__ float fmax3_nc(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float max8_nc(const float* v) {
+  return fmax_nc(fmax3_nc(fmax3_nc(fmax3_nc(v[0], v[1], v[2]), v[3], v[4]), v[5], v[6]), v[7]);
+}
+
 // Reductions over the four lanes l, l^16, l^32, l^48 that hold one head (VALU
 // row swaps; no LDS round trip).
 __device__ __forceinline__ float max_xg(float v) {
@@ -347,12 +356,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
     seg_row[j] = f / G::NSEG;
     seg_off[j] = (f - seg_row[j] * G::NSEG) * 16;
   }
-  auto issue = [&](uint32_t stage, int c) {
+  // Slots of the next chunk to gather, looked up one iteration ahead so that
+  // the loads never wait on an LDS round trip (rows past the valid count take
+  // the chunk's first row).
+  int slot[CNT0];
+  auto fetch_slots = [&](int c) {
     const int base = c * kKeys;
     const int nv = min(kKeys, n - base);
-    // all slot lookups first (rows past the valid count take the chunk's first
-    // row), so the loads below do not each wait on an LDS round trip
-    int slot[CNT0];
     if (nv == kKeys) {
 #pragma unroll
       for (int j = 0; j < CNT0; ++j) slot[j] = slot_list[base + seg_row[j]];
@@ -360,6 +370,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
 #pragma unroll
       for (int j = 0; j < CNT0; ++j) slot[j] = slot_list[base + (seg_row[j] < nv ? seg_row[j] : 0)];
     }
+  };
+  auto issue = [&](uint32_t stage, int c) {
+    (void)c;
 #pragma unroll
     for (int j = 0; j < CNT0; ++j) {
       if (j < my_cnt) {
@@ -376,11 +389,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
   // running max (log2 units) of this key half, per head; a finite sentinel
   // until the first valid key, so that exp2(-inf - m_run) is an exact 0
   float m_run = -1e30f;
-  float l_run = 0.0f;        // running sum over this lane's keys (4g + r)
-  int ne_run = 8;            // oacc = O * 2^(8 - ne_run)
+  float l_run = 0.0f;        // running sum over this lane's keys (4g + r), normalised
+  // P normaliser 2^ne_run: oacc and l_run hold O and l times 2^(8 - ne_run),
+  // and the exponent offset m_eff = m_run - (8 - ne_run) makes exp2(s - m_eff)
+  // come out already normalised
+  int ne_run = 8;
   int ne_hi = -126;
-  float x_lim = 256.0f;      // 2^ne_run: largest P * scale the normaliser takes
-  float inv_run = 1.0f;      // 2^(8 - ne_run)
+  float m_eff = -1e30f;
   f4 oacc[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) oacc[c] = f4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -392,8 +407,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
   // d0 + 8h; lane i then holds dim d0 + i of the group's 8 slots, byte k =
   // slot k), and the tile-pt scales of this lane's 8 keys (4g + r of blocks
   // 2ps and 2ps + 1).
-  long va[8];
-  float sc[8];
+  long va[2][8];
+  float sc[2][8];
   auto read_pv = [&](const uint8_t* stg, long* v, float* s) {
     const uint8_t* vsrc = stg + key_row(2 * ps + (k8 >> 2), 4 * g + (k8 & 3)) * RB + 128 * pt + 8 * h8;
 #pragma unroll
@@ -461,7 +476,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
   __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
   for (int c = 0; c < G::NST; ++c)
-    if (c < nch) issue(lds0 + (uint32_t)(c * G::STAGE), c);
+    if (c < nch) {
+      fetch_slots(c);
+      issue(lds0 + (uint32_t)(c * G::STAGE), c);
+    }
+  if (G::NST < nch) fetch_slots(G::NST);
   // chunk 0: wait for it (chunks 1 .. NST-1 stay in flight), score it, read its P.V operands
   if (nch > 0) {
     const int ahead = min(G::NST - 1, nch - 1);
@@ -470,9 +489,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
     else if (ahead == 2) { if (big) vm_barrier<2 * CNT0>(); else vm_barrier<2 * CNT1>(); }
     else { if (big) vm_barrier<3 * CNT0>(); else vm_barrier<3 * CNT1>(); }
     qk_finish(qk_mfma(qk_load(stages)), 0);
-    read_pv(stages, va, sc);
+    read_pv(stages, va[0], sc[0]);
   }
-  for (int c = 0; c < nch; ++c) {
+  // One chunk; its P.V operands are in (vc, scc), the next chunk's go to
+  // (vn, scn).  The loop runs two chunks per trip with the buffers swapped, so
+  // no operand is copied between registers.
+  auto step = [&](const int c, const long* vc, const float* scc, long* vn, float* scn) {
     // Chunk c+1 landed (this wave's loads issued after it: chunks c+2 ..
     // c+NST-1 that exist), and after the barrier chunk c's partial scores are
     // visible and nobody reads chunk c's stage any more.
@@ -480,23 +502,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
     if (ahead <= 0) vm_barrier<0>();
     else if (ahead == 1) { if (big) vm_barrier<CNT0>(); else vm_barrier<CNT1>(); }
     else { if (big) vm_barrier<2 * CNT0>(); else vm_barrier<2 * CNT1>(); }
-    const int cur = c % G::NST;
-    if (c + G::NST < nch) issue(lds0 + (uint32_t)(cur * G::STAGE), c + G::NST);
-
-    // Chunk c's partial scores are read first: LDS reads return in order, so
-    // the softmax then waits only for these, not for chunk c+1's operands.
+    // Chunk c's partial scores are read first, ahead of the gather issue:
+    // LDS reads return in order, so the softmax then waits only for these, and
+    // the issue runs while they are in flight.
     float4 u[2][2];
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
       for (int h = 0; h < 2; ++h) u[bb][h] = xs[c & 1][2 * ps + bb][h][lane];
+    const int cur = c % G::NST;
+    if (c + G::NST < nch) issue(lds0 + (uint32_t)(cur * G::STAGE), c + G::NST);
 
     // ---- next chunk's operands (for the last chunk: stale bytes, results unused) ----
     const uint8_t* nstg = stages + ((c + 1) % G::NST) * G::STAGE;
     const QkLoad nk = qk_load(nstg);
-    long va_n[8];
-    float sc_n[8];
-    read_pv(nstg, va_n, sc_n);
+    read_pv(nstg, vn, scn);
+    if (c + G::NST + 1 < nch) fetch_slots(c + G::NST + 1);
 
     // ---------------- softmax over keys 32ps + [0,32) of chunk c ----------------
     // An empty key half (last chunk) scores -inf throughout and adds exact zeros.
@@ -518,9 +539,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
     // 2^8, so p <= 256 and most chunks leave O's scale untouched.  Whether any
     // head moves is a per-lane test and a wave vote; only then does the
     // wavefront reduce across lanes.
-    float lmax = sv[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) lmax = fmaxf(lmax, sv[e]);
+    const float lmax = max8_nc(sv);
     const bool moved = __any(lmax > m_run + 8.0f);   // true on the first chunk with a valid key
     float alpha = 1.0f;
     if (moved) {
@@ -528,77 +547,77 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
       const float m_new = mloc > m_run + 8.0f ? mloc : m_run;
       alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 1 unless this head's max moved
       m_run = m_new;
+      m_eff = m_run - (float)(8 - ne_run);
     }
-    float p[8];
-    float psum = 0.0f;
+    // p * 2^(8 - ne_run) and (P * scale) * 2^(8 - ne_run), the P.V operand
+    float pn[8], y[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      p[e] = __builtin_amdgcn_exp2f(sv[e] - m_run);   // -inf -> exactly 0
-      psum += p[e];
+      pn[e] = __builtin_amdgcn_exp2f(sv[e] - m_eff);   // -inf -> exactly 0
+      y[e] = pn[e] * scc[e];            // padding rows: p = 0, scale finite (a copied row)
     }
-    l_run = l_run * alpha + psum;
-
-    // ---------------- P.V for tile pt ----------------
-    float x[8];
-    float xmax = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      x[e] = p[e] * sc[e];              // padding rows: p = 0, sc finite (a copied row)
-      xmax = fmaxf(xmax, x[e]);
-    }
-    // The normaliser 2^ne (oacc holds O * 2^(8 - ne_run), operands scaled into
-    // [0, 256]) changes only when the max moved or a product outgrows it;
-    // otherwise it is kept, which needs no cross-lane work.  It is set from the
-    // largest product since the max last moved (within 2^1), so e4m3 flushing
-    // drops only terms below 2^-17 of the largest one.
-    if (moved || __any(xmax > x_lim)) {
-      const float nm = max_xg(xmax);
+    float psum = ((pn[0] + pn[1]) + (pn[2] + pn[3])) + ((pn[4] + pn[5]) + (pn[6] + pn[7]));
+    // The normaliser changes only when the max moved or a product outgrows
+    // [0, 256]; otherwise it is kept, which needs no cross-lane work.  It is
+    // set from the largest product since the max last moved (within 2^1), so
+    // e4m3 flushing drops only terms below 2^-17 of the largest one.
+    const float ymax = max8_nc(y);
+    if (moved || __any(ymax > 256.0f)) {
+      const float nm = max_xg(ymax) * exp2_pow(ne_run - 8);   // largest P * scale
       int ne = 0;
       if (nm > 0.0f) {
         const uint32_t bits = __float_as_uint(nm);
         ne = (int)((bits >> 23) & 0xFF) - 127 + ((bits & 0x7FFFFF) ? 1 : 0);
-        ne = ne > 119 ? 119 : (ne < -118 ? -118 : ne);
+        ne = ne > 119 ? 119 : (ne < -96 ? -96 : ne);
       }
       // the normaliser stays within 2^96 of the largest one seen, which
-      // bounds oacc by 2^(11+9+8+96) < 2^128
+      // bounds oacc by 2^(11+9+8+96) < 2^128; with ne >= -96 the normalised p
+      // and l stay below 2^(8+8+96+9) per lane.  exp2 flushes results below
+      // 2^-126, so a key's p is dropped below 2^(ne - 134): below 2^-23 of the
+      // largest one while ne <= 111, i.e. tile maxima under about 2^110.
       ne_hi = ne > ne_hi ? ne : ne_hi;
       ne = ne < ne_hi - 96 ? ne_hi - 96 : ne;
       // a head whose max did not move keeps a normaliser that still fits
       if (alpha == 1.0f && ne <= ne_run) ne = ne_run;
-      const float resc = ldexpf(alpha, ne_run - ne);
+      const float f = exp2_pow(ne_run - ne);   // this chunk: old normaliser -> new
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] *= f;
+      psum *= f;
+      const float resc = alpha * f;            // O and l: old max and normaliser -> new
       ne_run = ne;
-      x_lim = exp2_pow(ne);
-      inv_run = exp2_pow(8 - ne);
+      m_eff = m_run - (float)(8 - ne);
       if (!__all(resc == 1.0f)) {
+        l_run *= resc;
 #pragma unroll
         for (int cc = 0; cc < 8; ++cc)
 #pragma unroll
           for (int r = 0; r < 4; ++r) oacc[cc][r] *= resc;
       }
     }
-    const float inv = inv_run;
+    l_run += psum;
     uint32_t h0, l0, h1, l1;
-    split_e4m3(x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv, h0, l0);
-    split_e4m3(x[4] * inv, x[5] * inv, x[6] * inv, x[7] * inv, h1, l1);
+    split_e4m3(y[0], y[1], y[2], y[3], h0, l0);
+    split_e4m3(y[4], y[5], y[6], y[7], h1, l1);
     const long bhi = pack64(h0, h1), blo = pack64(l0, l1);
     // next chunk's QK^T products, then this chunk's P.V, then the next scores
     const QkPart nq = qk_mfma(nk);
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc)
-      oacc[cc] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(va[cc], bhi, oacc[cc], 0, 0, 0);
+      oacc[cc] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(vc[cc], bhi, oacc[cc], 0, 0, 0);
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc)
-      oacc[cc] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(va[cc], blo, oacc[cc], 0, 0, 0);
+      oacc[cc] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(vc[cc], blo, oacc[cc], 0, 0, 0);
     if (c + 1 < nch) qk_finish(nq, c + 1);
-#pragma unroll
-    for (int cc = 0; cc < 8; ++cc) va[cc] = va_n[cc];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) sc[e] = sc_n[e];
+  };
+  for (int c = 0; c < nch; c += 2) {
+    step(c, va[0], sc[0], va[1], sc[1]);
+    if (c + 1 >= nch) break;
+    step(c + 1, va[1], sc[1], va[0], sc[0]);
   }
 
   // ---- combine the two key halves, then write ------------------------------
-  const float l_full = sum_xg(l_run);
   const float post = exp2_pow(ne_run - 8);
+  const float l_full = sum_xg(l_run) * post;
 #pragma unroll
   for (int cc = 0; cc < 8; ++cc)
 #pragma unroll
