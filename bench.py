@@ -9,11 +9,13 @@ pages, contexts U{1k..64k}.  `value` is algorithmic gathered KV bytes
 
 Caches are rotated across steps (several copies whose total exceeds the
 256 MB Infinity Cache), so each step's gathers come from HBM rather than a
-cache left warm by the previous step.  The timed steps replay one HIP graph
-per cache copy (writer + attention, captured from the library's launches;
-the library allocates nothing, so the capture holds only the kernels), which
-keeps host launch overhead out of the step time; the first replay is checked
-bit for bit against an eager step.  Per-kernel durations come from HIP events
+cache left warm by the previous step.  The timed steps replay HIP graphs
+captured from the library's launches (the library allocates nothing, so a
+capture holds only the kernels): one graph runs a whole rotation, one step
+per cache copy back to back, as a decode pass runs one layer after another,
+and one more graph runs the steps left over when K is not a multiple of the
+rotation.  That keeps host launch overhead out of the step time; each graph's
+replay is checked bit for bit against eager steps.  Per-kernel durations come from HIP events
 recorded on the library's stream around bursts of back-to-back launches.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras]
@@ -168,49 +170,65 @@ def main():
         smla.kv_write(new_lat, None, new_slots, c)
         smla.attn(q, c, idx, cfg["sm_scale"], 0, topk_capacity=W, out=out, lse=lse, workspace=ws)
 
-    # one graph per cache copy; eager launches if capture is unavailable
+    # The timed steps run as graphs of up to one rotation each (steps
+    # W + 7j .. W + 7j + 6 share one graph, as their cache copies repeat) plus
+    # one graph for the last K mod 7 steps; eager launches if capture is
+    # unavailable.
     launch_mode = "hip-graph"
-    graphs = []
+    rot = len(caches)
+    full = tail = None
+    n_full, n_tail = a.steps // rot, a.steps % rot
+
+    def capture(first, count):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(first, first + count):
+                step(i)
+        return g
+
     try:
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            for k in range(len(caches)):
+            for k in range(rot):
                 step(k)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         ref = out.clone()
-        for k in range(len(caches)):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                step(k)
-            graphs.append(g)
-        out.zero_()
-        graphs[0].replay()
-        torch.cuda.synchronize()
-        if not torch.equal(out, ref):
-            raise RuntimeError("graph replay differs from the eager step")
+        if n_full:
+            full = capture(a.warmup, rot)
+        if n_tail:
+            tail = capture(a.warmup + n_full * rot, n_tail)
+        for g in (full, tail):
+            if g is None:
+                continue
+            out.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            if not torch.equal(out, ref):
+                raise RuntimeError("graph replay differs from the eager steps")
     except Exception as exc:   # noqa: BLE001 - report and fall back to eager launches
         log(f"graph capture unavailable ({exc}); timing eager launches")
-        graphs, launch_mode = [], "eager"
-
-    def run_step(i):
-        if graphs:
-            graphs[i % len(graphs)].replay()
-        else:
-            step(i)
+        full = tail = None
+        launch_mode = "eager"
 
     for i in range(a.warmup):
-        run_step(i)
+        step(i)
     log(f"timing {a.steps} steps ({launch_mode})")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(a.steps):
-        run_step(a.warmup + i)
+    if launch_mode == "hip-graph":
+        for _ in range(n_full):
+            full.replay()
+        if tail is not None:
+            tail.replay()
+    else:
+        for i in range(a.steps):
+            step(a.warmup + i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / a.steps
-    del graphs
+    del full, tail
     # per-kernel durations: bursts of back-to-back launches, caches rotated
     attn_us = burst(lambda i: smla.attn(q, caches[i % len(caches)], idx, cfg["sm_scale"], 0,
                                         topk_capacity=W, out=out, lse=lse, workspace=ws),

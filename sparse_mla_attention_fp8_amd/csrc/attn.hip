@@ -558,23 +558,24 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
     }
     float psum = ((pn[0] + pn[1]) + (pn[2] + pn[3])) + ((pn[4] + pn[5]) + (pn[6] + pn[7]));
     // The normaliser changes only when the max moved or a product outgrows
-    // [0, 256]; otherwise it is kept, which needs no cross-lane work.  It is
-    // set from the largest product since the max last moved (within 2^1), so
-    // e4m3 flushing drops only terms below 2^-17 of the largest one.
+    // the e4m3 range (448); otherwise it is kept, which needs no cross-lane
+    // work.  It is set so that the largest product lands in (64, 128], which
+    // leaves room for 3.5x to 7x growth before the next change, and e4m3
+    // flushing drops only terms below 2^-16 of the largest one.
     const float ymax = max8_nc(y);
-    if (moved || __any(ymax > 256.0f)) {
+    if (moved || __any(ymax > 448.0f)) {
       const float nm = max_xg(ymax) * exp2_pow(ne_run - 8);   // largest P * scale
       int ne = 0;
       if (nm > 0.0f) {
         const uint32_t bits = __float_as_uint(nm);
-        ne = (int)((bits >> 23) & 0xFF) - 127 + ((bits & 0x7FFFFF) ? 1 : 0);
+        ne = (int)((bits >> 23) & 0xFF) - 127 + ((bits & 0x7FFFFF) ? 1 : 0) + 1;
         ne = ne > 119 ? 119 : (ne < -96 ? -96 : ne);
       }
       // the normaliser stays within 2^96 of the largest one seen, which
-      // bounds oacc by 2^(11+9+8+96) < 2^128; with ne >= -96 the normalised p
-      // and l stay below 2^(8+8+96+9) per lane.  exp2 flushes results below
+      // bounds oacc by 2^(11+9+9+96) < 2^128; with ne >= -96 the normalised p
+      // and l stay below 2^(8+8+96+11) per lane.  exp2 flushes results below
       // 2^-126, so a key's p is dropped below 2^(ne - 134): below 2^-23 of the
-      // largest one while ne <= 111, i.e. tile maxima under about 2^110.
+      // largest one while ne <= 111, i.e. tile maxima under about 2^109.
       ne_hi = ne > ne_hi ? ne : ne_hi;
       ne = ne < ne_hi - 96 ? ne_hi - 96 : ne;
       // a head whose max did not move keeps a normaliser that still fits
