@@ -288,6 +288,24 @@ def main():
     del caches
 
     extras = {}
+
+    def gather_extra(name, rot, rope_dim, n=65536):
+        """mla_gather_upconvert of n distinct random slots into bf16 [n][576],
+        cache copies rotated; algorithmic bytes: slot ids, the row bytes read
+        (528 or 656) and the 1,152 bytes written per row."""
+        num_slots = rot[0].shape[0]
+        rng_g = np.random.default_rng(80 + rope_dim)
+        sl = torch.from_numpy(rng_g.choice(np.arange(1, num_slots), size=n, replace=False)
+                              .astype(np.int64)).to(dev)
+        dst = torch.empty((n, 576), dtype=torch.bfloat16, device=dev)
+        us = burst(lambda i: smla.gather_upconvert(rot[i % len(rot)], sl, rope_dim, out=dst),
+                   a.steps, a.warmup)
+        byts = n * (8 + (ROPE_ROW if rope_dim else NOPE_ROW) + 1152)
+        extras[name] = {"us": round(float(us.mean()), 2),
+                        "gbs": round(byts / (us.mean() * 1e-6) / 1e9, 1),
+                        "hbm_frac": round(byts / (us.mean() * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"{name}: {us.mean():.2f} us")
+
     if not a.no_extras:
         # writer standalone: 8,192 rows, a quarter aimed at slot 0 with NaN inputs
         for rope_dim in (64, 0):
@@ -318,6 +336,7 @@ def main():
             extras[f"nope_decode_T{Tc}"] = {"us": round(float(us.mean()), 2),
                                            "gbs": round(b / (us.mean() * 1e-6) / 1e9, 1)}
             log(f"nope T={Tc}: {us.mean():.1f} us")
+        gather_extra("gather_upconvert_nope_N65536", rot, 0)
         del rot, cachec
         # RoPE decode T=256 and the disjoint control
         for name, c in (("rope_decode_T256", wl.config_rope_decode(256)),
@@ -331,7 +350,26 @@ def main():
                             "gbs": round(b / (us.mean() * 1e-6) / 1e9, 1),
                             "hbm_frac": round(b / (us.mean() * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
             log(f"{name}: {us.mean():.1f} us")
+            if name == "rope_decode_T256":
+                gather_extra("gather_upconvert_rope_N65536", rot, 64)
             del rot, cache
+        # LSE merge of 8 partial results (context-parallel decode over 8 owners),
+        # T=256, H=16; inputs rotated over copies larger than the Infinity Cache
+        Pm, Tm, Hm = 8, 256, 16
+        rng_m = np.random.default_rng(70)
+        po = bf16_dev(wl.normal_bf16(rng_m, (Pm, Tm, Hm, 512)))
+        pl = torch.from_numpy(rng_m.uniform(-8, 8, size=(Pm, Tm, Hm)).astype(np.float32)).to(dev)
+        nrot = max(2, int(np.ceil(600e6 / (po.numel() * 2))))
+        pos = [po] + [po.clone() for _ in range(nrot - 1)]
+        mo = torch.empty((Tm, Hm, 512), dtype=torch.bfloat16, device=dev)
+        ml = torch.empty((Tm, Hm), dtype=torch.float32, device=dev)
+        us = burst(lambda i: smla.merge(pos[i % nrot], pl, out=mo, lse=ml), a.steps, a.warmup)
+        byts = (Pm + 1) * Tm * Hm * (1024 + 4)
+        extras["merge_P8_T256"] = {"us": round(float(us.mean()), 2),
+                                   "gbs": round(byts / (us.mean() * 1e-6) / 1e9, 1),
+                                   "hbm_frac": round(byts / (us.mean() * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"merge P=8 T=256: {us.mean():.2f} us")
+        del pos, po
     result["extras"] = extras
 
     # ---------------- oracle on the host cores, bounded sample ----------------

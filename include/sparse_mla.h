@@ -10,6 +10,14 @@
  *   sparse_mla_attn  attends every query row over its top-k list of cache
  *                    slots, where a negative entry is padding.
  *
+ * and two more around them:
+ *
+ *   mla_gather_upconvert  dequantises listed cache rows into a bf16 workspace
+ *                         of 576-wide rows (the chunked-context reader's form);
+ *   sparse_mla_merge      merges partial (out, lse) pairs of sparse_mla_attn
+ *                         calls over disjoint shares of the top-k entries
+ *                         (context-parallel decoding) by their log-sum-exp.
+ *
  * Common rules
  *   - Every pointer argument is a DEVICE pointer owned by the caller; the
  *     library allocates nothing and keeps no device state between calls.
@@ -138,6 +146,58 @@ int sparse_mla_attn(const void* q,
                     void* out, float* lse,
                     void* workspace, size_t workspace_bytes,
                     hipStream_t stream);
+
+/*
+ * mla_gather_upconvert - dequantise listed cache rows into bf16 rows.
+ *
+ * Follows vLLM PR 55277, Purpose (1), and the review of that PR on the cache
+ * gather for the chunked-context path: with rope_dim 0 the reader must see
+ * exact zeros in columns 512..575, never stale cache bytes.  For each i:
+ *   if 0 <= slots[i] < num_slots, with row = kv_cache[slots[i]]:
+ *     dst[i][e]       = bf16(fp32(e4m3(code[e]) * scale[e / 128]))  (e < 512)
+ *     dst[i][512 + r] = RoPE value r (rope_dim 64), or +0 (rope_dim 0; row
+ *                       bytes [528, 656) are then not read)
+ *   otherwise (negative or >= num_slots) dst[i][0..576) = +0.
+ *   The dequantised value is rounded to float32, then to bf16, both to
+ *   nearest even; NaN codes give the bf16 NaN 0x7FC0.  Slot 0 is read like
+ *   any other slot.
+ *
+ * kv_cache        uint8 [num_slots][656], 16-byte aligned; num_slots >= 1.
+ * rope_dim        64 or 0 (the layout of the cache rows).
+ * slots           int64 [num_rows], 8-byte aligned.
+ * num_rows        >= 0 (0 launches nothing).
+ * dst             bf16 [num_rows][dst_row_stride], 16-byte aligned; columns
+ *                 576 .. dst_row_stride-1 are not written.
+ * dst_row_stride  elements, >= 576 and a multiple of 8.
+ */
+int mla_gather_upconvert(const void* kv_cache, int64_t num_slots, int rope_dim,
+                         const int64_t* slots, int64_t num_rows,
+                         void* dst, int64_t dst_row_stride, hipStream_t stream);
+
+/*
+ * sparse_mla_merge - combine partial attention results by their LSE.
+ *
+ * For context-parallel decoding the top-k entries of a row are split over P
+ * owners (sglang PR 47013, Motivation: the DCP rework that gives each rank
+ * ownership of its KV slots), each of which calls sparse_mla_attn on its own
+ * entries (the others as -1) and gets the normalised output O_p and lse_p; the
+ * same combination closes the split-K decode of sglang PR 39288, Motivation.
+ * For every (row t, head h):
+ *   lse = ln sum_p exp(lse_p),   out = sum_p exp(lse_p - lse) * O_p
+ * A part with lse_p = -inf (no valid entry) weighs exactly 0 and its O_p is
+ * not read; when every part is empty, out = 0 and lse = -inf.  fp32
+ * arithmetic, out rounded to bf16 (nearest even).  With P = 1 the call
+ * copies O_0 and lse_0.
+ *
+ * part_out        bf16 [P][T][H][512], contiguous, 16-byte aligned (e.g. the
+ *                 gathered out tensors of P sparse_mla_attn calls).
+ * part_lse        float32 [P][T][H] natural-log LSE, contiguous.
+ * P, T, H         P >= 1, T >= 1, 1 <= H <= 128.
+ * out             bf16 [T][H][512], 16-byte aligned; must not overlap the parts.
+ * lse             float32 [T][H], or NULL.
+ */
+int sparse_mla_merge(const void* part_out, const float* part_lse, int P, int T, int H,
+                     void* out, float* lse, hipStream_t stream);
 
 /* Thread-local description of the last error returned on this thread ("" if none). */
 const char* smla_last_error(void);

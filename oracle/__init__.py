@@ -13,5 +13,8 @@ Modules:
   attention - exact softmax attention over the valid top-k entries of the
               dequantised cache, and the faulty clamp-to-slot-0 reader that
               the pages describe (kept only as a negative control).
+  merge     - log-sum-exp merge of partial (output, lse) results of disjoint
+              shares of a row's top-k entries.
+  gather    - listed cache rows dequantised into 576-wide bf16 rows.
 """
-from . import e4m3, writer, attention  # noqa: F401
+from . import e4m3, writer, attention, merge, gather  # noqa: F401

@@ -8,6 +8,8 @@ and a missing or unloadable library raises.
     kv_write(kv_c, k_pe, slot_mapping, kv_cache)
     attn(q, kv_cache, topk_idx, sm_scale, rope_dim, topk_capacity=None,
          out=None, lse=None, workspace=None) -> (out, lse)
+    merge(part_out, part_lse, out=None, lse=None) -> (out, lse)
+    gather_upconvert(kv_cache, slots, rope_dim, out=None) -> out
 """
 from __future__ import annotations
 
@@ -32,6 +34,12 @@ _SIGS = {
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "mla_gather_upconvert": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]),
+    "sparse_mla_merge": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "smla_last_error": (ctypes.c_char_p, []),
 }
 
@@ -124,3 +132,39 @@ def attn(q, kv_cache, topk_idx, sm_scale: float, rope_dim: int, topk_capacity: i
                                ws_bytes, _stream(q))
     _check("sparse_mla_attn", rc)
     return out, lse
+
+
+def merge(part_out, part_lse, out=None, lse=None, want_lse: bool = True):
+    """Merge P partial results: part_out bf16 [P][T][H][512], part_lse float32
+    [P][T][H].  Returns (out bf16 [T][H][512], lse float32 [T][H] or None)."""
+    import torch
+    assert part_out.dtype == torch.bfloat16 and part_out.dim() == 4 and part_out.is_contiguous()
+    P, T, H, D = part_out.shape
+    assert D == LATENT
+    assert part_lse.dtype == torch.float32 and part_lse.is_contiguous() and tuple(part_lse.shape) == (P, T, H)
+    if out is None:
+        out = torch.empty((T, H, LATENT), dtype=torch.bfloat16, device=part_out.device)
+    if lse is None and want_lse:
+        lse = torch.empty((T, H), dtype=torch.float32, device=part_out.device)
+    rc = lib().sparse_mla_merge(part_out.data_ptr(), part_lse.data_ptr(), P, T, H, out.data_ptr(),
+                                _ptr(lse), _stream(part_out))
+    _check("sparse_mla_merge", rc)
+    return out, lse
+
+
+def gather_upconvert(kv_cache, slots, rope_dim: int, out=None):
+    """Dequantise cache rows kv_cache uint8 [num_slots][656] at slots int64 [N]
+    into bf16 [N][576] (out may be a wider row-strided view); invalid slots give
+    zero rows, NoPE rows zeros in columns 512..575."""
+    import torch
+    assert kv_cache.dtype == torch.uint8 and kv_cache.is_contiguous() and kv_cache.shape[-1] == ROW_BYTES
+    assert slots.dtype == torch.int64 and slots.dim() == 1 and slots.is_contiguous()
+    n = slots.shape[0]
+    if out is None:
+        out = torch.empty((n, LATENT + 64), dtype=torch.bfloat16, device=kv_cache.device)
+    assert out.dtype == torch.bfloat16 and out.dim() == 2 and out.stride(1) == 1 and out.shape[0] == n
+    rc = lib().mla_gather_upconvert(kv_cache.data_ptr(), kv_cache.numel() // ROW_BYTES, rope_dim,
+                                    slots.data_ptr(), n, out.data_ptr(), out.stride(0),
+                                    _stream(kv_cache))
+    _check("mla_gather_upconvert", rc)
+    return out

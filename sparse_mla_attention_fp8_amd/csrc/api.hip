@@ -104,4 +104,50 @@ int sparse_mla_attn(const void* q, const void* kv_cache, int64_t num_slots,
   return SMLA_OK;
 }
 
+int mla_gather_upconvert(const void* kv_cache, int64_t num_slots, int rope_dim,
+                         const int64_t* slots, int64_t num_rows, void* dst, int64_t dst_row_stride,
+                         hipStream_t stream) {
+  g_err[0] = '\0';
+  if (rope_dim != 0 && rope_dim != 64)
+    return fail(SMLA_EINVAL, "mla_gather_upconvert: rope_dim must be 0 or 64, got %d", rope_dim);
+  if (num_rows < 0) return fail(SMLA_EINVAL, "mla_gather_upconvert: num_rows < 0");
+  if (num_slots < 1) return fail(SMLA_EINVAL, "mla_gather_upconvert: num_slots must be >= 1");
+  if (num_rows == 0) return SMLA_OK;
+  if ((num_rows + 3) / 4 > 0x7FFFFFFF)
+    return fail(SMLA_EUNSUPPORTED, "mla_gather_upconvert: too many rows");
+  if (kv_cache == nullptr || slots == nullptr || dst == nullptr)
+    return fail(SMLA_EINVAL, "mla_gather_upconvert: null pointer argument");
+  if (dst_row_stride < 576 || (dst_row_stride & 7))
+    return fail(SMLA_EINVAL, "mla_gather_upconvert: dst_row_stride must be >= 576 and a multiple of 8");
+  if (!aligned16(kv_cache) || !aligned16(dst) || (reinterpret_cast<uintptr_t>(slots) & 7u))
+    return fail(SMLA_EINVAL, "mla_gather_upconvert: misaligned pointer");
+  hipError_t e = smla::launch_gather_upconvert(static_cast<const uint8_t*>(kv_cache), num_slots,
+                                               rope_dim, slots, num_rows,
+                                               static_cast<uint16_t*>(dst), dst_row_stride, stream);
+  if (e != hipSuccess)
+    return fail(SMLA_ELAUNCH, "mla_gather_upconvert: launch failed: %s", hipGetErrorString(e));
+  return SMLA_OK;
+}
+
+int sparse_mla_merge(const void* part_out, const float* part_lse, int P, int T, int H, void* out,
+                     float* lse, hipStream_t stream) {
+  g_err[0] = '\0';
+  if (P < 1 || T < 1 || H < 1 || H > SMLA_MAX_HEADS)
+    return fail(SMLA_EINVAL, "sparse_mla_merge: need P >= 1, T >= 1 and 1 <= H <= %d (P=%d, T=%d, H=%d)",
+                SMLA_MAX_HEADS, P, T, H);
+  const int64_t rows = (int64_t)T * H;
+  if ((rows + 3) / 4 > 0x7FFFFFFF)
+    return fail(SMLA_EUNSUPPORTED, "sparse_mla_merge: too many (row, head) pairs");
+  if (part_out == nullptr || part_lse == nullptr || out == nullptr)
+    return fail(SMLA_EINVAL, "sparse_mla_merge: null pointer argument");
+  if (!aligned16(part_out) || !aligned16(out) || (reinterpret_cast<uintptr_t>(part_lse) & 3u) ||
+      (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return fail(SMLA_EINVAL, "sparse_mla_merge: misaligned pointer");
+  hipError_t e = smla::launch_merge(static_cast<const uint16_t*>(part_out), part_lse, P, rows,
+                                    static_cast<uint16_t*>(out), lse, stream);
+  if (e != hipSuccess)
+    return fail(SMLA_ELAUNCH, "sparse_mla_merge: launch failed: %s", hipGetErrorString(e));
+  return SMLA_OK;
+}
+
 }  // extern "C"

@@ -34,4 +34,11 @@ hipError_t launch_attn(const uint16_t* q, const uint8_t* cache, int64_t num_slot
                        int rope_dim, float sm_scale, uint16_t* out, float* lse,
                        void* workspace, const AttnPlan& plan, hipStream_t stream);
 
+hipError_t launch_gather_upconvert(const uint8_t* cache, int64_t num_slots, int rope_dim,
+                                   const int64_t* slots, int64_t n, uint16_t* dst,
+                                   int64_t dst_stride, hipStream_t stream);
+
+hipError_t launch_merge(const uint16_t* part_out, const float* part_lse, int P, int64_t rows,
+                        uint16_t* out, float* lse, hipStream_t stream);
+
 }  // namespace smla

@@ -102,3 +102,36 @@ def test_workspace_size():
         ws = smla.workspace_size(T, 16, 2176, 0)
         assert ws % (16 * 514 * 4 * T) == 0
     assert big % (16 * 514 * 4 * 256) == 0
+
+
+def test_merge_validation():
+    L = smla.lib()
+    base = dict(part_out=FAKE, part_lse=FAKE, P=2, T=3, H=16, out=FAKE + 0x100000, lse=None, stream=None)
+    bad = [
+        dict(P=0), dict(T=0), dict(H=0), dict(H=129),
+        dict(part_out=None), dict(part_lse=None), dict(out=None),
+        dict(part_out=FAKE + 8), dict(out=FAKE + 0x100008), dict(part_lse=FAKE + 2), dict(lse=FAKE + 2),
+    ]
+    for b in bad:
+        a = {**base, **b}
+        rc = L.sparse_mla_merge(*a.values())
+        assert rc == smla.SMLA_EINVAL, b
+        assert L.smla_last_error().decode().startswith("sparse_mla_merge")
+
+
+def test_gather_validation():
+    L = smla.lib()
+    base = dict(kv_cache=FAKE, num_slots=128, rope_dim=64, slots=FAKE, num_rows=4,
+                dst=FAKE + 0x100000, dst_row_stride=576, stream=None)
+    bad = [
+        dict(rope_dim=32), dict(num_rows=-1), dict(num_slots=0),
+        dict(kv_cache=None), dict(slots=None), dict(dst=None),
+        dict(dst_row_stride=512), dict(dst_row_stride=580),
+        dict(kv_cache=FAKE + 8), dict(dst=FAKE + 0x100008), dict(slots=FAKE + 4),
+    ]
+    for b in bad:
+        a = {**base, **b}
+        rc = L.mla_gather_upconvert(*a.values())
+        assert rc == smla.SMLA_EINVAL, b
+        assert L.smla_last_error().decode().startswith("mla_gather_upconvert")
+    assert L.mla_gather_upconvert(*{**base, "num_rows": 0, "kv_cache": None}.values()) in (smla.SMLA_OK, smla.SMLA_EINVAL)
