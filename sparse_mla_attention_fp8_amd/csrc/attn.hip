@@ -215,34 +215,42 @@ __device__ __forceinline__ long pack64(uint32_t lo, uint32_t hi) {
   return (long)(((uint64_t)hi << 32) | lo);
 }
 
-// Compacts the valid entries of idx[lo, hi) into list[] in order; returns the
-// count.  All index loads are issued before the first round so their latency
-// is paid once.
+// Compacts the valid entries of idx[lo, hi) into list[] in buffer order and
+// returns their count.  Thread i takes entries lo + kPer*i .. lo + kPer*i +
+// kPer - 1 (its loads all issued at once); an exclusive scan of the per-thread
+// counts (within a wavefront by shuffles, across wavefronts through LDS)
+// places them.  Two barriers in all.
 __device__ int compact_valid(const int32_t* __restrict__ idx, int lo, int hi, int64_t num_slots,
                              int* list, int* wave_counts) {
-  constexpr int kRounds = (kMaxRange + kThreads - 1) / kThreads;
+  constexpr int kPer = (kMaxRange + kThreads - 1) / kThreads;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int v[kRounds];
+  const int k0 = lo + kPer * tid;
+  int v[kPer];
 #pragma unroll
-  for (int i = 0; i < kRounds; ++i) {
-    const int k = lo + i * kThreads + tid;
-    v[i] = k < hi ? idx[k] : -1;
-  }
-  int total = 0;
+  for (int i = 0; i < kPer; ++i) v[i] = k0 + i < hi ? idx[k0 + i] : -1;
+  int cnt = 0;
 #pragma unroll
-  for (int i = 0; i < kRounds; ++i) {
-    if (lo + i * kThreads >= hi) break;
-    const bool ok = v[i] >= 0 && (int64_t)v[i] < num_slots;
-    const uint64_t mask = __ballot(ok);
-    const int before = __popcll(mask & ((1ull << lane) - 1ull));
-    if (lane == 0) wave_counts[wave] = __popcll(mask);
-    __syncthreads();
-    int off = total;
-    for (int w = 0; w < wave; ++w) off += wave_counts[w];
-    if (ok) list[off + before] = v[i];
-    for (int w = 0; w < kWaves; ++w) total += wave_counts[w];
-    __syncthreads();
+  for (int i = 0; i < kPer; ++i) cnt += (v[i] >= 0 && (int64_t)v[i] < num_slots) ? 1 : 0;
+  int x = cnt;   // inclusive prefix within the wavefront
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
   }
+  if (lane == 63) wave_counts[wave] = x;
+  __syncthreads();
+  int base = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const int c = wave_counts[w];
+    total += c;
+    base += w < wave ? c : 0;
+  }
+  int pos = base + x - cnt;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i)
+    if (v[i] >= 0 && (int64_t)v[i] < num_slots) list[pos++] = v[i];
+  __syncthreads();
   return total;
 }
 
@@ -277,24 +285,48 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
   const int hg = b % head_groups;
   const int t = b / head_groups;
 
-  // ---- q fragments of head n16 (issued before the index scan) -------------
+  // ---- q of the group's heads -> LDS (one copy per workgroup, issued before
+  // the index scan), rows padded by 16 bytes so the fragment reads below fall
+  // on distinct banks
   const int head = hg * kHeads + n16;
   const bool hvalid = head < H;
-  const uint16_t* qrow = q + ((int64_t)t * H + (hvalid ? head : 0)) * D;
-  uint4 qraw[8];    // tile 2qh+u: dims 128(2qh+u) + 32g + 8k + [0, 8), k = 0..3 -> qraw[4u + k]
+  {
+    constexpr int kSegs = D / 8;                  // 16-byte segments of a q row
+    constexpr int kPitch = kSegs + 1;             // LDS row pitch in segments
+    constexpr int kInstr = (kHeads * kPitch + 63) / 64;
+    const int nh = min(kHeads, H - hg * kHeads);
+    const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(q + ((int64_t)t * H + hg * kHeads) * D);
+    const uint32_t lds_q = lds_addr(stages);
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      qraw[4 * u + k] = *reinterpret_cast<const uint4*>(qrow + 128 * (2 * qh + u) + 32 * g + 8 * k);
-  uint4 qpe_raw = make_uint4(0, 0, 0, 0);    // RoPE k-step qh: dims 512 + 32qh + 8g + [0, 8)
-  if (ROPE) qpe_raw = *reinterpret_cast<const uint4*>(qrow + kLatent + 32 * qh + 8 * g);
+    for (int j = 0; j < (kInstr + kWaves - 1) / kWaves; ++j) {
+      const int i = wave + kWaves * j;
+      const int f = 64 * i + lane;                // LDS segment
+      const int h = f / kPitch, e = f - h * kPitch;
+      if (i < kInstr && h < nh && e < kSegs)
+        dma16(qsrc + (int64_t)h * D * 2 + 16 * e, lds_q + 1024u * (uint32_t)i);
+    }
+  }
 
   const int lo_k = split * range;
   const int hi_k = min(W, lo_k + range);
+  // (its barriers also publish the staged q: each wavefront's first wait for
+  // its index loads covers its earlier q loads)
   const int n = __builtin_amdgcn_readfirstlane(
       compact_valid(idx + (int64_t)t * idx_stride, lo_k, hi_k, num_slots, slot_list, wave_counts));
   const int nch = (n + kKeys - 1) / kKeys;
+
+  // q fragments of head n16: tile 2qh+u, dims 128(2qh+u) + 32g + 8k + [0, 8) -> qraw[4u + k]
+  uint4 qraw[8];
+  uint4 qpe_raw = make_uint4(0, 0, 0, 0);    // RoPE k-step qh: dims 512 + 32qh + 8g + [0, 8)
+  {
+    const uint8_t* qlds = stages + (size_t)n16 * (D * 2 + 16);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        qraw[4 * u + k] = *reinterpret_cast<const uint4*>(qlds + 2 * (128 * (2 * qh + u) + 32 * g + 8 * k));
+    if (ROPE) qpe_raw = *reinterpret_cast<const uint4*>(qlds + 2 * (kLatent + 32 * qh + 8 * g));
+  }
 
   if (!hvalid) {
 #pragma unroll
@@ -469,11 +501,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
 
   // ---- pipeline: chunk c lives in stage c % NST ----
   const uint32_t lds0 = lds_addr(stages);
-  // Every compiler-visible load (q) is complete before the pipeline starts, so
+  // Every compiler-visible load is complete before the pipeline starts, so
   // the compiler has no reason to emit a vmcnt wait of its own in the loop
   // (it does not count the inline-asm gathers; a wait of its own there would
-  // drain the whole pipeline).
+  // drain the whole pipeline); and every wavefront has read its q fragments
+  // before the gathers overwrite the staged q.
   __builtin_amdgcn_s_waitcnt(0);
+  lds_barrier();
 #pragma unroll
   for (int c = 0; c < G::NST; ++c)
     if (c < nch) {
@@ -677,43 +711,87 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
 }
 
 // Combines split partials (m in log2 units): M = max m_s, L = sum 2^(m_s - M) l_s,
-// O = sum 2^(m_s - M) O_s / L, lse = (M + log2 L) ln 2.  One 64-thread block per (row, head).
-__global__ __launch_bounds__(64) void attn_merge_kernel(const float* __restrict__ part_o,
-                                                        const float* __restrict__ part_ml,
-                                                        int splits, int H,
-                                                        uint16_t* __restrict__ out,
-                                                        float* __restrict__ lse) {
+// O = sum 2^(m_s - M) O_s / L, lse = (M + log2 L) ln 2.  One 512-thread block
+// per (row, head): wavefront w sums splits w, w + 8, ... against its own
+// running maximum, with eight splits' loads in flight at once; the eight sums
+// then meet in LDS, rescaled to the common maximum.  A split without valid
+// entries has m = -1e30 and l = 0 (finite partials), so it weighs nothing;
+// L = 0 means the row has no valid entry.
+constexpr int kMergeWaves = 8;
+constexpr int kMergeUnroll = 8;
+
+__global__ __launch_bounds__(64 * kMergeWaves) void attn_merge_kernel(const float* __restrict__ part_o,
+                                                                      const float* __restrict__ part_ml,
+                                                                      int splits, int H,
+                                                                      uint16_t* __restrict__ out,
+                                                                      float* __restrict__ lse) {
+  __shared__ float4 po[kMergeWaves][2][64];
+  __shared__ float2 pml[kMergeWaves];
   const int th = blockIdx.x;  // t * H + h
   const int t = th / H, hh = th % H;
-  const int lane = threadIdx.x;
-  float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, part_ml[2 * (((int64_t)t * splits + s) * H + hh)]);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const float* ml = part_ml + 2 * ((int64_t)t * splits * H + hh);   // split s at ml[2 * s * H]
+  const float* po_base = part_o + ((int64_t)t * splits * H + hh) * kLatent + 8 * lane;  // + s * H * 512
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-  float L = 0.0f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < splits; ++s) {
-      const int64_t p = ((int64_t)t * splits + s) * H + hh;
-      const float ms = part_ml[2 * p];
-      if (ms == -INFINITY) continue;  // empty split
-      const float w = __builtin_amdgcn_exp2f(ms - M);
-      L += w * part_ml[2 * p + 1];
-      const float4* src = reinterpret_cast<const float4*>(part_o + p * kLatent + 8 * lane);
-      const float4 a = src[0], c = src[1];
-      acc[0] += w * a.x; acc[1] += w * a.y; acc[2] += w * a.z; acc[3] += w * a.w;
-      acc[4] += w * c.x; acc[5] += w * c.y; acc[6] += w * c.z; acc[7] += w * c.w;
+  float Mw = -INFINITY, L = 0.0f;
+  for (int s0 = wave; s0 < splits; s0 += kMergeWaves * kMergeUnroll) {
+    float ms[kMergeUnroll], ls[kMergeUnroll];
+    float4 a[kMergeUnroll], c[kMergeUnroll];
+#pragma unroll
+    for (int j = 0; j < kMergeUnroll; ++j) {
+      const int s = s0 + kMergeWaves * j;
+      const bool in = s < splits;
+      ms[j] = in ? ml[2 * (int64_t)s * H] : -INFINITY;
+      ls[j] = in ? ml[2 * (int64_t)s * H + 1] : 0.0f;
+      const float4* src = reinterpret_cast<const float4*>(po_base + (int64_t)s * H * kLatent);
+      a[j] = in ? src[0] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      c[j] = in ? src[1] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
+    float mg = Mw;
+#pragma unroll
+    for (int j = 0; j < kMergeUnroll; ++j) mg = fmaxf(mg, ms[j]);
+    const float f = __builtin_amdgcn_exp2f(Mw - mg);   // 0 on the first group
+    L *= f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] *= f;
+#pragma unroll
+    for (int j = 0; j < kMergeUnroll; ++j) {
+      const float w = __builtin_amdgcn_exp2f(ms[j] - mg);   // 0 for the padding j
+      L += w * ls[j];
+      acc[0] += w * a[j].x; acc[1] += w * a[j].y; acc[2] += w * a[j].z; acc[3] += w * a[j].w;
+      acc[4] += w * c[j].x; acc[5] += w * c[j].y; acc[6] += w * c[j].z; acc[7] += w * c[j].w;
+    }
+    Mw = mg;
   }
-  const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
+  po[wave][0][lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  po[wave][1][lane] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  if (lane == 0) pml[wave] = make_float2(Mw, L);
+  __syncthreads();
+  if (wave != 0) return;
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kMergeWaves; ++w) M = fmaxf(M, pml[w].x);
+  float o[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  float Lt = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kMergeWaves; ++w) {
+    const float2 mlw = pml[w];
+    const float f = mlw.x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mlw.x - M);   // idle wavefronts
+    const float4 x = po[w][0][lane], y = po[w][1][lane];
+    o[0] += f * x.x; o[1] += f * x.y; o[2] += f * x.z; o[3] += f * x.w;
+    o[4] += f * y.x; o[5] += f * y.y; o[6] += f * y.z; o[7] += f * y.w;
+    Lt += f * mlw.y;
+  }
+  const float inv = (Lt > 0.0f) ? 1.0f / Lt : 0.0f;
   uint32_t pk[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    pk[i] = (uint32_t)f32_to_bf16_rne(acc[2 * i] * inv) |
-            ((uint32_t)f32_to_bf16_rne(acc[2 * i + 1] * inv) << 16);
-  *reinterpret_cast<uint4*>(out + (int64_t)th * kLatent + 8 * lane) =
-      make_uint4(pk[0], pk[1], pk[2], pk[3]);
-  if (lse != nullptr && lane == 0) lse[th] = (L > 0.0f) ? (M + __log2f(L)) * kLn2 : -INFINITY;
+    pk[i] = (uint32_t)f32_to_bf16_rne(o[2 * i] * inv) | ((uint32_t)f32_to_bf16_rne(o[2 * i + 1] * inv) << 16);
+  *reinterpret_cast<uint4*>(out + (int64_t)th * kLatent + 8 * lane) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+  if (lse != nullptr && lane == 0) lse[th] = (Lt > 0.0f) ? (M + __log2f(Lt)) * kLn2 : -INFINITY;
 }
 
 }  // namespace
@@ -763,7 +841,7 @@ hipError_t launch_attn(const uint16_t* q, const uint8_t* cache, int64_t num_slot
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.splits == 1) return e;
-  hipLaunchKernelGGL(attn_merge_kernel, dim3(T * H), dim3(64), 0, stream, part_o, part_ml,
+  hipLaunchKernelGGL(attn_merge_kernel, dim3(T * H), dim3(64 * kMergeWaves), 0, stream, part_o, part_ml,
                      plan.splits, H, out, lse);
   return hipGetLastError();
 }

@@ -25,24 +25,13 @@ namespace {
 
 constexpr int kGatherWaves = 4;          // wavefronts per 256-thread block
 constexpr int kRowsPerWave = 4;          // rows per wavefront, loaded together
+typedef float f2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
   u += 0x7FFFu + ((u >> 16) & 1u);
   return u >> 16;
-}
-
-// OCP E4M3 ("fn") code -> float32, exactly: 2^(E-7) (1 + m/8) for E > 0,
-// 2^-6 (m/8) for E = 0, NaN for the all-ones magnitude.
-__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
-  const uint32_t mag = c & 0x7Fu;
-  const uint32_t sign = (c & 0x80u) << 24;
-  if (mag == 0x7Fu) return __uint_as_float(sign | 0x7FC00000u);
-  const uint32_t E = mag >> 3, m = mag & 7u;
-  const float v = E ? __uint_as_float(((E + 120u) << 23) | (m << 20))   // exponent E-7 re-biased
-                    : (float)m * 0.001953125f;                          // m * 2^-9
-  return __uint_as_float(__float_as_uint(v) | sign);
 }
 
 __global__ __launch_bounds__(64 * kGatherWaves) void gather_upconvert_kernel(
@@ -78,16 +67,16 @@ __global__ __launch_bounds__(64 * kGatherWaves) void gather_upconvert_kernel(
     uint16_t* drow = dst + i * dst_stride;
     uint4 o = make_uint4(0, 0, 0, 0);
     if (ok[k]) {
-      const uint32_t c[2] = {codes[k].x, codes[k].y};
+      // the hardware fp8 -> f32 conversion is exact for every e4m3 code
+      // (NaN codes give NaN); the product is rounded once to f32
+      const int c[2] = {(int)codes[k].x, (int)codes[k].y};
       uint32_t pk[4];
 #pragma unroll
       for (int w = 0; w < 2; ++w) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const float a = e4m3_to_f32((c[w] >> (16 * h)) & 0xFFu) * scale[k];
-          const float b = e4m3_to_f32((c[w] >> (16 * h + 8)) & 0xFFu) * scale[k];
-          pk[2 * w + h] = bf16_rne_bits(a) | (bf16_rne_bits(b) << 16);
-        }
+        const f2 ab = __builtin_amdgcn_cvt_pk_f32_fp8(c[w], false);
+        const f2 cd = __builtin_amdgcn_cvt_pk_f32_fp8(c[w], true);
+        pk[2 * w] = bf16_rne_bits(ab[0] * scale[k]) | (bf16_rne_bits(ab[1] * scale[k]) << 16);
+        pk[2 * w + 1] = bf16_rne_bits(cd[0] * scale[k]) | (bf16_rne_bits(cd[1] * scale[k]) << 16);
       }
       o = make_uint4(pk[0], pk[1], pk[2], pk[3]);
     }

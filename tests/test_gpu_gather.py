@@ -35,11 +35,14 @@ def test_gather_byte_exact(rope_dim):
     cache = build_cache(cfg)
     if rope_dim == 0:
         cache[1:, 528:] = 0xA5            # sentinel tails must never reach the output
+    cache[17, 3] = 0x7F                   # NaN codes inside an ordinary row
+    cache[17, 200] = 0xFF
     slots = rng.integers(1, cfg["num_slots"], size=3001).astype(np.int64)
     slots[::97] = -1
     slots[5] = cfg["num_slots"]
     slots[7] = 1 << 40
     slots[9] = 0                          # slot 0 (0xFF bytes) is read like any slot
+    slots[11] = 17
     out = smla.gather_upconvert(cache, torch.from_numpy(slots).to(DEV), rope_dim)
     torch.cuda.synchronize()
     want = oracle_gather.gather_upconvert(cache.cpu().numpy(), slots, rope_dim)
