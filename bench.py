@@ -353,6 +353,36 @@ def main():
             if name == "rope_decode_T256":
                 gather_extra("gather_upconvert_rope_N65536", rot, 64)
             del rot, cache
+        # BF16 KV cache: NoPE decode T=256 over rows of 512 bf16 values
+        cb = wl.config_nope_decode(256)
+        log("generating bf16_nope_decode_T256")
+        cacheb = torch.zeros((cb["num_slots"], 512), dtype=torch.bfloat16, device=dev)
+        smla.kv_write_bf16(bf16_dev(cb["latent"]), None, torch.from_numpy(cb["slots"]).to(dev), cacheb)
+        nrb = max(2, int(np.ceil(600e6 / (cacheb.numel() * 2))))
+        rotb = [cacheb] + [cacheb.clone() for _ in range(nrb - 1)]
+        qb_ = bf16_dev(cb["q"])
+        idxb = torch.from_numpy(cb["idx"]).to(dev)
+        ob = torch.empty((256, 16, 512), dtype=torch.bfloat16, device=dev)
+        lb = torch.empty((256, 16), dtype=torch.float32, device=dev)
+        us = burst(lambda i: smla.attn_bf16(qb_, rotb[i % nrb], idxb, cb["sm_scale"], out=ob, lse=lb),
+                   a.steps, a.warmup)
+        b = gathered(cb, 1024)
+        extras["bf16_nope_decode_T256"] = {"us": round(float(us.mean()), 2),
+                                           "gbs": round(b / (us.mean() * 1e-6) / 1e9, 1),
+                                           "hbm_frac": round(b / (us.mean() * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"bf16_nope_decode_T256: {us.mean():.1f} us")
+        wb = wl.config_writer(N=8192, rope_dim=0)
+        wcache = torch.zeros((wb["cache"].shape[0], 512), dtype=torch.bfloat16, device=dev)
+        wlat = bf16_dev(wb["latent"])
+        wsl = torch.from_numpy(wb["slots"]).to(dev)
+        us = burst(lambda i: smla.kv_write_bf16(wlat, None, wsl, wcache), a.steps, a.warmup)
+        written = int((wb["slots"] > 0).sum())
+        extras["writer_bf16_8192_rope0"] = {"us": round(float(us.mean()), 3),
+                                            "rows_per_us": round(8192 / us.mean(), 1),
+                                            "gbs": round((written * (1024 + 1024 + 8) + (8192 - written) * 8)
+                                                         / (us.mean() * 1e-6) / 1e9, 1)}
+        log(f"writer bf16 rope0: {us.mean():.2f} us")
+        del rotb, cacheb, wcache
         # LSE merge of 8 partial results (context-parallel decode over 8 owners),
         # T=256, H=16; inputs rotated over copies larger than the Infinity Cache
         Pm, Tm, Hm = 8, 256, 16

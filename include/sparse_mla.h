@@ -10,6 +10,10 @@
  *   sparse_mla_attn  attends every query row over its top-k list of cache
  *                    slots, where a negative entry is padding.
  *
+ * the same two over a BF16 KV cache (rows of bf16 values, no quantisation):
+ *
+ *   mla_kv_write_bf16, sparse_mla_attn_bf16;
+ *
  * and two more around them:
  *
  *   mla_gather_upconvert  dequantises listed cache rows into a bf16 workspace
@@ -146,6 +150,43 @@ int sparse_mla_attn(const void* q,
                     void* out, float* lse,
                     void* workspace, size_t workspace_bytes,
                     hipStream_t stream);
+
+/*
+ * mla_kv_write_bf16 - store MLA KV rows into a BF16 KV cache.
+ *
+ * The BF16 cache of sglang PR 47013, Speed Tests (its timed writer stores rows
+ * of 512 bf16 values; the end-to-end runs there use a BF16 KV cache): row
+ * slot of kv_cache (bf16 [num_slots][512 + rope_dim]) receives kv_c[i][0..512)
+ * and, with rope_dim 64, k_pe[i][0..64), unchanged.  The slot rule of
+ * mla_kv_write applies: slot 0, negative slots and slots >= num_slots are
+ * dropped and their inputs never read.  Arguments as for mla_kv_write, except
+ * kv_cache: bf16 [num_slots][512 + rope_dim], 16-byte aligned.
+ */
+int mla_kv_write_bf16(const void* kv_c, int64_t kv_c_row_stride,
+                      const void* k_pe, int64_t k_pe_row_stride,
+                      int rope_dim,
+                      const int64_t* slot_mapping, int64_t num_rows,
+                      void* kv_cache, int64_t num_slots,
+                      hipStream_t stream);
+
+/*
+ * sparse_mla_attn_bf16 - sparse MLA attention over a BF16 KV cache.
+ *
+ * The computation of sparse_mla_attn with K_j[e] = the bf16 value stored at
+ * kv_cache[j][e] (no dequantisation).  This build supports NoPE rows only:
+ * rope_dim 0, kv_cache bf16 [num_slots][512]; rope_dim 64 returns
+ * SMLA_EUNSUPPORTED (a 1,152-byte row does not fit the kernel's two LDS
+ * stages).  All other arguments, the padding rules, the workspace (same size
+ * as sparse_mla_attn_workspace_size) and the error behaviour are those of
+ * sparse_mla_attn.
+ */
+int sparse_mla_attn_bf16(const void* q,
+                         const void* kv_cache, int64_t num_slots,
+                         const int32_t* topk_idx, int64_t idx_row_stride, int topk_capacity,
+                         int T, int H, int rope_dim, float sm_scale,
+                         void* out, float* lse,
+                         void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
 
 /*
  * mla_gather_upconvert - dequantise listed cache rows into bf16 rows.

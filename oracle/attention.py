@@ -68,10 +68,26 @@ def sparse_mla_attn(q_bits: np.ndarray, cache: np.ndarray, idx: np.ndarray, widt
     cache: uint8 [num_slots][656]; idx: int32 [T][>= width].
     Returns (out float64 [T][H][512], lse float64 [T][H]); `rows` restricts the
     computation to the listed query rows (others are left NaN)."""
+    return _attend(q_bits, cache.shape[0], lambda v: dequant_rows(cache, v, rope_dim), idx, width,
+                   rope_dim, sm_scale, rows)
+
+
+def sparse_mla_attn_bf16(q_bits: np.ndarray, cache_bits: np.ndarray, idx: np.ndarray, width: int,
+                         rope_dim: int, sm_scale: float, rows=None):
+    """The same attention over a BF16 KV cache (sglang PR 47013, Speed Tests):
+    cache_bits uint16 [num_slots][512 + rope_dim] holds the K rows themselves,
+    K[j][e] = bf16 value e of row j (A2 without dequantisation)."""
+    assert cache_bits.shape[1] == LATENT + rope_dim
+    return _attend(q_bits, cache_bits.shape[0],
+                   lambda v: _bf16_to_f64(cache_bits[np.asarray(v, dtype=np.int64)]), idx, width,
+                   rope_dim, sm_scale, rows)
+
+
+def _attend(q_bits, num_slots, k_rows, idx, width, rope_dim, sm_scale, rows):
+    """A1, A3-A6 over K rows given by k_rows(valid slots) -> float64 [n][512 + rope_dim]."""
     q = _bf16_to_f64(q_bits)
     T, H, D = q.shape
     assert D == LATENT + rope_dim
-    num_slots = cache.shape[0]
     out = np.full((T, H, LATENT), np.nan)
     lse = np.full((T, H), np.nan)
     for t in (range(T) if rows is None else rows):
@@ -80,7 +96,7 @@ def sparse_mla_attn(q_bits: np.ndarray, cache: np.ndarray, idx: np.ndarray, widt
             out[t] = 0.0
             lse[t] = -np.inf
             continue
-        k = dequant_rows(cache, v, rope_dim)                             # A2
+        k = k_rows(v)                                                    # A2
         s = float(sm_scale) * (q[t] @ k.T)                               # A3  [H][n]
         m = s.max(axis=1, keepdims=True)
         e = np.exp(s - m)

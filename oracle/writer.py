@@ -89,3 +89,23 @@ def kv_write(cache: np.ndarray, latent_bits: np.ndarray, rope_bits: np.ndarray |
                            None if rope_bits is None else np.asarray(rope_bits)[kept])
         cache[slots[kept]] = rows
     return keep
+
+
+def kv_write_bf16(cache_bits: np.ndarray, latent_bits: np.ndarray, rope_bits: np.ndarray | None,
+                  slots: np.ndarray) -> np.ndarray:
+    """BF16 KV cache (sglang PR 47013, Speed Tests: rows of 512 bf16 values):
+    cache_bits uint16 [num_slots][512 + rope_dim] receives each kept row's bf16
+    values unchanged, in place; the slot rule W1 and W6 are those of the
+    quantised cache.  Returns the keep mask."""
+    num_slots, width = cache_bits.shape
+    rope_dim = 0 if rope_bits is None else 64
+    assert width == 512 + rope_dim and cache_bits.dtype == np.uint16
+    slots = np.asarray(slots, dtype=np.int64)
+    keep = (slots >= 1) & (slots < num_slots)
+    kept = np.nonzero(keep)[0]
+    if kept.size:
+        row = np.asarray(latent_bits, dtype=np.uint16)[kept, :512]
+        if rope_dim:
+            row = np.concatenate([row, np.asarray(rope_bits, dtype=np.uint16)[kept, :64]], axis=1)
+        cache_bits[slots[kept]] = row
+    return keep

@@ -10,6 +10,8 @@ and a missing or unloadable library raises.
          out=None, lse=None, workspace=None) -> (out, lse)
     merge(part_out, part_lse, out=None, lse=None) -> (out, lse)
     gather_upconvert(kv_cache, slots, rope_dim, out=None) -> out
+    kv_write_bf16(kv_c, k_pe, slot_mapping, kv_cache_bf16)
+    attn_bf16(q, kv_cache_bf16, topk_idx, sm_scale, ...) -> (out, lse)
 """
 from __future__ import annotations
 
@@ -31,6 +33,13 @@ _SIGS = {
     "sparse_mla_attn_workspace_size": (ctypes.c_size_t, [
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]),
     "sparse_mla_attn": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "mla_kv_write_bf16": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]),
+    "sparse_mla_attn_bf16": (ctypes.c_int, [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
@@ -168,3 +177,47 @@ def gather_upconvert(kv_cache, slots, rope_dim: int, out=None):
                                     _stream(kv_cache))
     _check("mla_gather_upconvert", rc)
     return out
+
+
+def kv_write_bf16(kv_c, k_pe, slot_mapping, kv_cache) -> None:
+    """Store bf16 rows kv_c [N][>=512] (+ k_pe [N][>=64] or None) into the BF16
+    cache kv_cache bf16 [num_slots][512 + rope_dim] at slot_mapping int64 [N]."""
+    import torch
+    assert kv_c.dtype == torch.bfloat16 and kv_c.dim() == 2 and kv_c.stride(1) == 1
+    assert slot_mapping.dtype == torch.int64 and slot_mapping.is_contiguous()
+    rope_dim, pe_stride = 0, 0
+    if k_pe is not None:
+        assert k_pe.dtype == torch.bfloat16 and k_pe.dim() == 2 and k_pe.stride(1) == 1
+        rope_dim, pe_stride = 64, k_pe.stride(0)
+    assert kv_cache.dtype == torch.bfloat16 and kv_cache.is_contiguous()
+    assert kv_cache.shape[-1] == LATENT + rope_dim
+    rc = lib().mla_kv_write_bf16(kv_c.data_ptr(), kv_c.stride(0), _ptr(k_pe), pe_stride, rope_dim,
+                                 slot_mapping.data_ptr(), kv_c.shape[0], kv_cache.data_ptr(),
+                                 kv_cache.numel() // (LATENT + rope_dim), _stream(kv_cache))
+    _check("mla_kv_write_bf16", rc)
+
+
+def attn_bf16(q, kv_cache, topk_idx, sm_scale: float, topk_capacity: int | None = None,
+              out=None, lse=None, workspace=None, want_lse: bool = True):
+    """Sparse MLA attention over the BF16 cache kv_cache bf16 [num_slots][512]
+    (NoPE).  q bf16 [T][H][512]; topk_idx int32 [T][>=W]."""
+    import torch
+    assert q.dtype == torch.bfloat16 and q.dim() == 3 and q.is_contiguous() and q.shape[2] == LATENT
+    assert kv_cache.dtype == torch.bfloat16 and kv_cache.is_contiguous() and kv_cache.shape[-1] == LATENT
+    assert topk_idx.dtype == torch.int32 and topk_idx.dim() == 2 and topk_idx.stride(1) == 1
+    T, H, _ = q.shape
+    W = topk_idx.shape[1] if topk_capacity is None else int(topk_capacity)
+    if out is None:
+        out = torch.empty((T, H, LATENT), dtype=torch.bfloat16, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    need = workspace_size(T, H, W, 0)
+    if need and (workspace is None or workspace.numel() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().sparse_mla_attn_bf16(q.data_ptr(), kv_cache.data_ptr(), kv_cache.numel() // LATENT,
+                                    topk_idx.data_ptr(), topk_idx.stride(0), W, T, H, 0,
+                                    float(sm_scale), out.data_ptr(), _ptr(lse), _ptr(workspace),
+                                    ws_bytes, _stream(q))
+    _check("sparse_mla_attn_bf16", rc)
+    return out, lse

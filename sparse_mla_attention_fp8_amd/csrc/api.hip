@@ -60,6 +60,37 @@ int mla_kv_write(const void* kv_c, int64_t kv_c_row_stride, const void* k_pe,
   return SMLA_OK;
 }
 
+int mla_kv_write_bf16(const void* kv_c, int64_t kv_c_row_stride, const void* k_pe,
+                      int64_t k_pe_row_stride, int rope_dim, const int64_t* slot_mapping,
+                      int64_t num_rows, void* kv_cache, int64_t num_slots, hipStream_t stream) {
+  g_err[0] = '\0';
+  if (rope_dim != 0 && rope_dim != 64)
+    return fail(SMLA_EINVAL, "mla_kv_write_bf16: rope_dim must be 0 or 64, got %d", rope_dim);
+  if (num_rows < 0) return fail(SMLA_EINVAL, "mla_kv_write_bf16: num_rows < 0");
+  if (num_slots < 1) return fail(SMLA_EINVAL, "mla_kv_write_bf16: num_slots must be >= 1");
+  if (num_rows == 0) return SMLA_OK;
+  if (kv_c == nullptr || slot_mapping == nullptr || kv_cache == nullptr)
+    return fail(SMLA_EINVAL, "mla_kv_write_bf16: null pointer argument");
+  if (rope_dim == 64 && k_pe == nullptr)
+    return fail(SMLA_EINVAL, "mla_kv_write_bf16: k_pe is NULL with rope_dim 64");
+  if (rope_dim == 0 && k_pe != nullptr)
+    return fail(SMLA_EINVAL, "mla_kv_write_bf16: k_pe must be NULL with rope_dim 0");
+  if (kv_c_row_stride < smla::kLatent || (kv_c_row_stride & 7))
+    return fail(SMLA_EINVAL, "mla_kv_write_bf16: kv_c_row_stride must be >= 512 and a multiple of 8");
+  if (rope_dim == 64 && (k_pe_row_stride < 64 || (k_pe_row_stride & 7)))
+    return fail(SMLA_EINVAL, "mla_kv_write_bf16: k_pe_row_stride must be >= 64 and a multiple of 8");
+  if (!aligned16(kv_c) || !aligned16(kv_cache) || (k_pe && !aligned16(k_pe)) ||
+      (reinterpret_cast<uintptr_t>(slot_mapping) & 7u))
+    return fail(SMLA_EINVAL, "mla_kv_write_bf16: misaligned pointer");
+  hipError_t e = smla::launch_kv_write_bf16(
+      static_cast<const uint16_t*>(kv_c), kv_c_row_stride, static_cast<const uint16_t*>(k_pe),
+      k_pe_row_stride, rope_dim, slot_mapping, num_rows, static_cast<uint16_t*>(kv_cache),
+      num_slots, stream);
+  if (e != hipSuccess)
+    return fail(SMLA_ELAUNCH, "mla_kv_write_bf16: launch failed: %s", hipGetErrorString(e));
+  return SMLA_OK;
+}
+
 size_t sparse_mla_attn_workspace_size(int T, int H, int topk_capacity, int rope_dim) {
   if (T < 1 || T > kMaxRows || H < 1 || H > SMLA_MAX_HEADS || topk_capacity < 1 ||
       (rope_dim != 0 && rope_dim != 64))
@@ -101,6 +132,45 @@ int sparse_mla_attn(const void* q, const void* kv_cache, int64_t num_slots,
                                    static_cast<uint16_t*>(out), lse, workspace, plan, stream);
   if (e != hipSuccess)
     return fail(SMLA_ELAUNCH, "sparse_mla_attn: launch failed: %s", hipGetErrorString(e));
+  return SMLA_OK;
+}
+
+int sparse_mla_attn_bf16(const void* q, const void* kv_cache, int64_t num_slots,
+                         const int32_t* topk_idx, int64_t idx_row_stride, int topk_capacity, int T,
+                         int H, int rope_dim, float sm_scale, void* out, float* lse,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_err[0] = '\0';
+  if (rope_dim != 0 && rope_dim != 64)
+    return fail(SMLA_EINVAL, "sparse_mla_attn_bf16: rope_dim must be 0 or 64, got %d", rope_dim);
+  if (rope_dim == 64)
+    return fail(SMLA_EUNSUPPORTED, "sparse_mla_attn_bf16: only NoPE rows (rope_dim 0) are supported");
+  if (T < 1 || H < 1 || H > SMLA_MAX_HEADS)
+    return fail(SMLA_EINVAL, "sparse_mla_attn_bf16: need T >= 1 and 1 <= H <= %d (T=%d, H=%d)",
+                SMLA_MAX_HEADS, T, H);
+  if (T > kMaxRows)
+    return fail(SMLA_EUNSUPPORTED, "sparse_mla_attn_bf16: at most %d query rows per call", kMaxRows);
+  if (topk_capacity < 1 || idx_row_stride < topk_capacity)
+    return fail(SMLA_EINVAL, "sparse_mla_attn_bf16: need 1 <= topk_capacity <= idx_row_stride");
+  if (num_slots < 1) return fail(SMLA_EINVAL, "sparse_mla_attn_bf16: num_slots must be >= 1");
+  if (!isfinite(sm_scale)) return fail(SMLA_EINVAL, "sparse_mla_attn_bf16: sm_scale is not finite");
+  if (q == nullptr || kv_cache == nullptr || topk_idx == nullptr || out == nullptr)
+    return fail(SMLA_EINVAL, "sparse_mla_attn_bf16: null pointer argument");
+  if (!aligned16(q) || !aligned16(kv_cache) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(topk_idx) & 3u) || (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return fail(SMLA_EINVAL, "sparse_mla_attn_bf16: misaligned pointer");
+  const smla::AttnPlan plan = smla::plan_attn(T, H, topk_capacity, rope_dim);
+  if (plan.workspace > 0) {
+    if (workspace == nullptr || workspace_bytes < plan.workspace)
+      return fail(SMLA_EWORKSPACE, "sparse_mla_attn_bf16: workspace of %zu bytes needed, got %zu",
+                  plan.workspace, workspace == nullptr ? (size_t)0 : workspace_bytes);
+    if (!aligned16(workspace)) return fail(SMLA_EINVAL, "sparse_mla_attn_bf16: misaligned workspace");
+  }
+  hipError_t e = smla::launch_attn_bf16(static_cast<const uint16_t*>(q),
+                                        static_cast<const uint16_t*>(kv_cache), num_slots, topk_idx,
+                                        idx_row_stride, topk_capacity, T, H, sm_scale,
+                                        static_cast<uint16_t*>(out), lse, workspace, plan, stream);
+  if (e != hipSuccess)
+    return fail(SMLA_ELAUNCH, "sparse_mla_attn_bf16: launch failed: %s", hipGetErrorString(e));
   return SMLA_OK;
 }
 

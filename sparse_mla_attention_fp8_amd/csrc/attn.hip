@@ -710,6 +710,298 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// BF16 KV cache: rows are bf16 [num_slots][512] (1,024 bytes, NoPE), the cache
+// form of sglang PR 47013, Speed Tests (its timed writer stores 512 bf16
+// values per row, and its end-to-end runs use a BF16 KV cache).  The same
+// pipeline as attn_mfma_kernel, with:
+//   * rows staged at a 1,040-byte LDS pitch (one idle lane per 65 of the
+//     gather lays out a 16-byte pad), so rows start 4 banks apart;
+//   * QK^T on v_mfma_f32_16x16x32_bf16 (8 K-steps of 32 dims per 256-dim
+//     half), q used as is;
+//   * P.V on v_mfma_f32_16x16x32_bf16 with P rounded once to bf16 and V^T
+//     read by ds_read_b64_tr_b16: within each 16-lane group, lane 4a+b gets
+//     element b of the 8-byte pieces that lanes a, a+4, a+8, a+12 address;
+//   * no tile scales and no normaliser (bf16 P covers the whole range).
+constexpr int kB16Pitch = 1040;                  // LDS bytes per staged row
+constexpr int kB16Stage = kKeys * kB16Pitch;     // 66,560
+constexpr int kB16NST = 2;                       // one chunk in flight while one computes
+constexpr int kB16Instr = kKeys * (kB16Pitch / 16) / 64;   // 65 x 1-KB loads per chunk
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+
+template <bool SMALL>
+__global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ cache, int64_t num_slots,
+    const int32_t* __restrict__ idx, int64_t idx_stride, int W, int H, float sm_scale_log2,
+    int range, int splits, int head_groups, uint16_t* __restrict__ out, float* __restrict__ lse,
+    float* __restrict__ part_o, float* __restrict__ part_ml) {
+  __shared__ __align__(16) uint8_t stages[kB16NST * kB16Stage];
+  __shared__ int slot_list[kMaxRange];
+  __shared__ __align__(16) float4 xs[2][4][2][64];
+  __shared__ int wave_counts[kWaves];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n16 = lane & 15, g = lane >> 4;
+  const int qb = wave >> 1, qh = wave & 1;
+  const int pt = wave >> 1, ps = wave & 1;
+  int b = blockIdx.x;
+  const int split = b % splits;
+  b /= splits;
+  const int hg = b % head_groups;
+  const int t = b / head_groups;
+  const int head = hg * kHeads + n16;
+  const bool hvalid = head < H;
+  const uint8_t* cache8 = reinterpret_cast<const uint8_t*>(cache);
+
+  // ---- q of the group's heads -> LDS at the same padded pitch -------------
+  {
+    const int nh = min(kHeads, H - hg * kHeads);
+    const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(q + ((int64_t)t * H + hg * kHeads) * kLatent);
+    const uint32_t lds_q = lds_addr(stages);
+#pragma unroll
+    for (int j = 0; j < (17 + kWaves - 1) / kWaves; ++j) {
+      const int i = wave + kWaves * j;           // 16 rows x 65 segments = 1,040 -> 17 loads
+      const int f = 64 * i + lane;
+      const int h = f / 65, e = f - h * 65;
+      if (i < 17 && h < nh && e < 64) dma16(qsrc + (int64_t)h * 1024 + 16 * e, lds_q + 1024u * (uint32_t)i);
+    }
+  }
+  const int lo_k = split * range;
+  const int hi_k = min(W, lo_k + range);
+  const int n = __builtin_amdgcn_readfirstlane(
+      compact_valid(idx + (int64_t)t * idx_stride, lo_k, hi_k, num_slots, slot_list, wave_counts));
+  const int nch = (n + kKeys - 1) / kKeys;
+  // q fragments (B operand of the K-steps of half qh): dims 256qh + 32s + 8g + [0, 8)
+  bf16x8 qf[8];
+  {
+    const uint8_t* qlds = stages + (size_t)n16 * kB16Pitch;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      uint4 v = *reinterpret_cast<const uint4*>(qlds + 2 * (256 * qh + 32 * s + 8 * g));
+      if (!hvalid) v = make_uint4(0, 0, 0, 0);
+      qf[s] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  // ---- gather geometry: load i = wave + 8j covers LDS segments 64i + lane;
+  // segment f is row f / 65, piece f % 65 (piece 64 is the pad, not loaded)
+  constexpr int CNT0 = (kB16Instr + kWaves - 1) / kWaves;   // 9
+  constexpr int CNT1 = kB16Instr / kWaves;                  // 8
+  const bool big = wave < kB16Instr % kWaves;
+  const int my_cnt = big ? CNT0 : CNT1;
+  int seg_row[CNT0], seg_off[CNT0];
+#pragma unroll
+  for (int j = 0; j < CNT0; ++j) {
+    const int f = j < my_cnt ? 64 * (wave + kWaves * j) + lane : 64;   // unused loads: a pad piece
+    seg_row[j] = f / 65;
+    seg_off[j] = (f - seg_row[j] * 65) * 16;                          // 1,024 = the pad
+  }
+  int slot[CNT0];
+  auto fetch_slots = [&](int c) {
+    const int base = c * kKeys;
+    const int nv = min(kKeys, n - base);
+    if (nv == kKeys) {
+#pragma unroll
+      for (int j = 0; j < CNT0; ++j) slot[j] = slot_list[base + seg_row[j]];
+    } else {
+#pragma unroll
+      for (int j = 0; j < CNT0; ++j) slot[j] = slot_list[base + (seg_row[j] < nv ? seg_row[j] : 0)];
+    }
+  };
+  auto issue = [&](uint32_t stage) {
+#pragma unroll
+    for (int j = 0; j < CNT0; ++j) {
+      if (j < my_cnt && seg_off[j] < 1024) {
+        const uint32_t lds = stage + 1024u * (uint32_t)(wave + kWaves * j);
+        if (SMALL) {
+          dma16_sbase(cache8, (uint32_t)slot[j] * 1024u + (uint32_t)seg_off[j], lds);
+        } else {
+          dma16(cache8 + (int64_t)slot[j] * 1024 + seg_off[j], lds);
+        }
+      }
+    }
+  };
+
+  float m_run = -1e30f;
+  float l_run = 0.0f;
+  f4 oacc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) oacc[c] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // P.V operands of a chunk: V^T of tile pt, dim block cc (16 dims), keys K =
+  // 8g + j <-> row key_row(2ps + (j >> 2), 4g + (j & 3)); two transposed reads
+  // per block (j = 0..3, then 4..7).  Lane 4a+b of each 16-lane group addresses
+  // row (4g + (lane>>2 & 3)) of the block pair at dims d0 + 4(lane & 3).
+  const int tr_a = n16 & 3, tr_k = n16 >> 2;
+  bf16x8 va[2][8];
+  auto read_pv = [&](const uint8_t* stg, bf16x8* v) {
+    const uint8_t* r0 = stg + key_row(2 * ps, 4 * g + tr_k) * kB16Pitch + 2 * (128 * pt + 4 * tr_a);
+    const uint8_t* r1 = stg + key_row(2 * ps + 1, 4 * g + tr_k) * kB16Pitch + 2 * (128 * pt + 4 * tr_a);
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) {
+      const v4s x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(r0 + 32 * cc));
+      const v4s x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(r1 + 32 * cc));
+      typedef short v8s __attribute__((ext_vector_type(8)));
+      const v8s w = v8s{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+      v[cc] = __builtin_bit_cast(bf16x8, w);
+    }
+  };
+  // QK^T of a chunk: keys 16qb + [0,16) (row n16 of block qb), dims half qh;
+  // K-steps s = 0..7 cover dims 256qh + 32s + [0, 32)
+  struct QkLoad { bf16x8 a[8]; };
+  auto qk_load = [&](const uint8_t* stg) {
+    QkLoad o;
+    const uint8_t* krow = stg + key_row(qb, n16) * kB16Pitch + 2 * (256 * qh + 8 * g);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) o.a[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(krow + 64 * s));
+    return o;
+  };
+  auto qk_mfma = [&](const QkLoad& k) {
+    const f4 z4 = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    f4 e = z4, d = z4;   // two chains of four K-steps
+#pragma unroll
+    for (int s = 0; s < 8; s += 2) {
+      e = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k.a[s], qf[s], e, 0, 0, 0);
+      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k.a[s + 1], qf[s + 1], d, 0, 0, 0);
+    }
+    return e + d;
+  };
+  auto qk_finish = [&](const f4 acc, int c) {
+    xs[c & 1][qb][qh][lane] = make_float4(acc[0] * sm_scale_log2, acc[1] * sm_scale_log2,
+                                          acc[2] * sm_scale_log2, acc[3] * sm_scale_log2);
+  };
+
+  const uint32_t lds0 = lds_addr(stages);
+  __builtin_amdgcn_s_waitcnt(0);
+  lds_barrier();                                   // staged q read by every wavefront
+#pragma unroll
+  for (int c = 0; c < kB16NST; ++c)
+    if (c < nch) {
+      fetch_slots(c);
+      issue(lds0 + (uint32_t)(c * kB16Stage));
+    }
+  if (kB16NST < nch) fetch_slots(kB16NST);
+  if (nch > 0) {
+    if (nch > 1) { if (big) vm_barrier<CNT0>(); else vm_barrier<CNT1>(); }
+    else vm_barrier<0>();
+    qk_finish(qk_mfma(qk_load(stages)), 0);
+    read_pv(stages, va[0]);
+  }
+  auto step = [&](const int c, const bf16x8* vc, bf16x8* vn) {
+    // chunk c+1 landed (nothing issued after it), chunk c's scores visible,
+    // chunk c's stage free
+    vm_barrier<0>();
+    float4 u[2][2];
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) u[bb][h] = xs[c & 1][2 * ps + bb][h][lane];
+    const int cur = c % kB16NST;
+    if (c + kB16NST < nch) issue(lds0 + (uint32_t)(cur * kB16Stage));
+    const uint8_t* nstg = stages + ((c + 1) % kB16NST) * kB16Stage;
+    const QkLoad nk = qk_load(nstg);
+    read_pv(nstg, vn);
+    if (c + kB16NST + 1 < nch) fetch_slots(c + kB16NST + 1);
+
+    const int nv = min(kKeys, n - c * kKeys);
+    float sv[8];
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      sv[4 * bb + 0] = u[bb][0].x + u[bb][1].x;
+      sv[4 * bb + 1] = u[bb][0].y + u[bb][1].y;
+      sv[4 * bb + 2] = u[bb][0].z + u[bb][1].z;
+      sv[4 * bb + 3] = u[bb][0].w + u[bb][1].w;
+    }
+    if (nv < kKeys) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (key_row(2 * ps + (e >> 2), 4 * g + (e & 3)) >= nv) sv[e] = -INFINITY;
+    }
+    const float lmax = max8_nc(sv);
+    if (__any(lmax > m_run + 8.0f)) {
+      const float mloc = max_xg(lmax);
+      const float m_new = mloc > m_run + 8.0f ? mloc : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      if (!__all(alpha == 1.0f)) {
+        l_run *= alpha;
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) oacc[cc][r] *= alpha;
+      }
+    }
+    float pn[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pn[e] = __builtin_amdgcn_exp2f(sv[e] - m_run);   // -inf -> 0
+    l_run += ((pn[0] + pn[1]) + (pn[2] + pn[3])) + ((pn[4] + pn[5]) + (pn[6] + pn[7]));
+    bf16x8 pb;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pb[e] = (__bf16)pn[e];
+    const f4 nq = qk_mfma(nk);
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) oacc[cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vc[cc], pb, oacc[cc], 0, 0, 0);
+    if (c + 1 < nch) qk_finish(nq, c + 1);
+  };
+  for (int c = 0; c < nch; c += 2) {
+    step(c, va[0], va[1]);
+    if (c + 1 >= nch) break;
+    step(c + 1, va[1], va[0]);
+  }
+
+  // ---- combine the two key halves, then write ------------------------------
+  const float l_full = sum_xg(l_run);
+  lds_barrier();
+  float4* mo = reinterpret_cast<float4*>(stages);
+  float2* ml = reinterpret_cast<float2*>(stages + 4 * 64 * 128);
+  const int slot4 = pt * 64 + lane;
+  if (ps == 1) {
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc)
+      mo[cc * 256 + slot4] = make_float4(oacc[cc][0], oacc[cc][1], oacc[cc][2], oacc[cc][3]);
+    ml[slot4] = make_float2(m_run, l_full);
+  }
+  lds_barrier();
+  if (ps == 1 || !hvalid) return;
+  const float2 o1 = ml[slot4];
+  const float M = fmaxf(m_run, o1.x);
+  const float w0 = __builtin_amdgcn_exp2f(m_run - M);
+  const float w1 = __builtin_amdgcn_exp2f(o1.x - M);
+  const float L = w0 * l_full + w1 * o1.y;
+  const int dim0 = 128 * pt + 4 * g;
+  if (splits == 1) {
+    const float il = L > 0.0f ? 1.0f / L : 0.0f;
+    uint16_t* dst = out + ((int64_t)t * H + head) * kLatent + dim0;
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) {
+      const float4 u = mo[cc * 256 + slot4];
+      const float o4[4] = {w0 * oacc[cc][0] + w1 * u.x, w0 * oacc[cc][1] + w1 * u.y,
+                           w0 * oacc[cc][2] + w1 * u.z, w0 * oacc[cc][3] + w1 * u.w};
+      const uint32_t lo2 = (uint32_t)f32_to_bf16_rne(o4[0] * il) | ((uint32_t)f32_to_bf16_rne(o4[1] * il) << 16);
+      const uint32_t hi2 = (uint32_t)f32_to_bf16_rne(o4[2] * il) | ((uint32_t)f32_to_bf16_rne(o4[3] * il) << 16);
+      *reinterpret_cast<uint2*>(dst + 16 * cc) = make_uint2(lo2, hi2);
+    }
+    if (lse != nullptr && pt == 0 && g == 0)
+      lse[(int64_t)t * H + head] = L > 0.0f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+  } else {
+    const int64_t pidx = ((int64_t)t * splits + split) * H + head;
+    float* dst = part_o + pidx * kLatent + dim0;
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) {
+      const float4 u = mo[cc * 256 + slot4];
+      *reinterpret_cast<float4*>(dst + 16 * cc) =
+          make_float4(w0 * oacc[cc][0] + w1 * u.x, w0 * oacc[cc][1] + w1 * u.y,
+                      w0 * oacc[cc][2] + w1 * u.z, w0 * oacc[cc][3] + w1 * u.w);
+    }
+    if (pt == 0 && g == 0) {
+      part_ml[2 * pidx] = M;
+      part_ml[2 * pidx + 1] = L;
+    }
+  }
+}
+
 // Combines split partials (m in log2 units): M = max m_s, L = sum 2^(m_s - M) l_s,
 // O = sum 2^(m_s - M) O_s / L, lse = (M + log2 L) ln 2.  One 512-thread block
 // per (row, head): wavefront w sums splits w, w + 8, ... against its own
@@ -839,6 +1131,32 @@ hipError_t launch_attn(const uint16_t* q, const uint8_t* cache, int64_t num_slot
   } else {
     if (small) go(attn_mfma_kernel<0, true>); else go(attn_mfma_kernel<0, false>);
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || plan.splits == 1) return e;
+  hipLaunchKernelGGL(attn_merge_kernel, dim3(T * H), dim3(64 * kMergeWaves), 0, stream, part_o, part_ml,
+                     plan.splits, H, out, lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bf16(const uint16_t* q, const uint16_t* cache, int64_t num_slots,
+                            const int32_t* idx, int64_t idx_stride, int W, int T, int H,
+                            float sm_scale, uint16_t* out, float* lse, void* workspace,
+                            const AttnPlan& plan, hipStream_t stream) {
+  float* part_o = nullptr;
+  float* part_ml = nullptr;
+  if (plan.splits > 1) {
+    part_o = static_cast<float*>(workspace);
+    part_ml = part_o + (size_t)T * plan.splits * H * kLatent;
+  }
+  const int64_t blocks = (int64_t)plan.splits * T * plan.head_groups;
+  const float sl2 = sm_scale * kLog2e;
+  const bool small = num_slots <= (int64_t)(0xFFFFFFFFull / 1024);   // row byte offsets fit 32 bits
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, q, cache, num_slots,
+                       idx, idx_stride, W, H, sl2, plan.range, plan.splits, plan.head_groups, out,
+                       lse, part_o, part_ml);
+  };
+  if (small) go(attn_bf16_kernel<true>); else go(attn_bf16_kernel<false>);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.splits == 1) return e;
   hipLaunchKernelGGL(attn_merge_kernel, dim3(T * H), dim3(64 * kMergeWaves), 0, stream, part_o, part_ml,

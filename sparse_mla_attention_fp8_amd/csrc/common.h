@@ -19,6 +19,11 @@ hipError_t launch_kv_write(const uint16_t* kv_c, int64_t kv_c_stride, const uint
                            int64_t num_rows, uint8_t* cache, int64_t num_slots,
                            hipStream_t stream);
 
+hipError_t launch_kv_write_bf16(const uint16_t* kv_c, int64_t kv_c_stride, const uint16_t* k_pe,
+                                int64_t k_pe_stride, int rope_dim, const int64_t* slot_mapping,
+                                int64_t num_rows, uint16_t* cache, int64_t num_slots,
+                                hipStream_t stream);
+
 // Launch plan of the attention call; a pure function of the sizes, shared by
 // the workspace query and the launch so the two always agree.
 struct AttnPlan {
@@ -33,6 +38,11 @@ hipError_t launch_attn(const uint16_t* q, const uint8_t* cache, int64_t num_slot
                        const int32_t* idx, int64_t idx_stride, int W, int T, int H,
                        int rope_dim, float sm_scale, uint16_t* out, float* lse,
                        void* workspace, const AttnPlan& plan, hipStream_t stream);
+
+hipError_t launch_attn_bf16(const uint16_t* q, const uint16_t* cache, int64_t num_slots,
+                            const int32_t* idx, int64_t idx_stride, int W, int T, int H,
+                            float sm_scale, uint16_t* out, float* lse, void* workspace,
+                            const AttnPlan& plan, hipStream_t stream);
 
 hipError_t launch_gather_upconvert(const uint8_t* cache, int64_t num_slots, int rope_dim,
                                    const int64_t* slots, int64_t n, uint16_t* dst,

@@ -93,7 +93,40 @@ __global__ __launch_bounds__(256) void kv_write_kernel(
     *reinterpret_cast<float*>(dst + kScaleOff + 4 * (lane >> 4)) = scale;
 }
 
+// BF16 cache rows (sglang PR 47013, Speed Tests: rows of 512 bf16 values):
+// row = bf16 [512 + rope_dim], written as is, with the same slot rule.  One
+// wavefront per row: lane l moves latent values 8l..8l+7, lanes 0..7 the RoPE
+// values.
+__global__ __launch_bounds__(64 * kRowsPerBlock) void kv_write_bf16_kernel(
+    const uint16_t* __restrict__ kv_c, int64_t kv_c_stride, const uint16_t* __restrict__ k_pe,
+    int64_t k_pe_stride, int rope_dim, const int64_t* __restrict__ slot_mapping, int64_t num_rows,
+    uint16_t* __restrict__ cache, int64_t num_slots) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= num_rows) return;
+  const int64_t slot = slot_mapping[row];
+  if (slot <= 0 || slot >= num_slots) return;   // dropped before any input load
+  uint16_t* dst = cache + slot * (int64_t)(kLatent + rope_dim);
+  const uint4 v = reinterpret_cast<const uint4*>(kv_c + row * kv_c_stride)[lane];
+  uint4 pe = make_uint4(0, 0, 0, 0);
+  if (rope_dim != 0 && lane < 8) pe = reinterpret_cast<const uint4*>(k_pe + row * k_pe_stride)[lane];
+  reinterpret_cast<uint4*>(dst)[lane] = v;
+  if (rope_dim != 0 && lane < 8) reinterpret_cast<uint4*>(dst + kLatent)[lane] = pe;
+}
+
 }  // namespace
+
+hipError_t launch_kv_write_bf16(const uint16_t* kv_c, int64_t kv_c_stride, const uint16_t* k_pe,
+                                int64_t k_pe_stride, int rope_dim, const int64_t* slot_mapping,
+                                int64_t num_rows, uint16_t* cache, int64_t num_slots,
+                                hipStream_t stream) {
+  if (num_rows == 0) return hipSuccess;
+  const int64_t blocks = (num_rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  hipLaunchKernelGGL(kv_write_bf16_kernel, dim3((unsigned)blocks), dim3(64 * kRowsPerBlock), 0,
+                     stream, kv_c, kv_c_stride, k_pe, k_pe_stride, rope_dim, slot_mapping, num_rows,
+                     cache, num_slots);
+  return hipGetLastError();
+}
 
 hipError_t launch_kv_write(const uint16_t* kv_c, int64_t kv_c_stride, const uint16_t* k_pe,
                            int64_t k_pe_stride, int rope_dim, const int64_t* slot_mapping,
