@@ -400,6 +400,19 @@ def main():
                                    "hbm_frac": round(byts / (us.mean() * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
         log(f"merge P=8 T=256: {us.mean():.2f} us")
         del pos, po
+        # page re-split: all 512 pages of a 131,072-slot pool of 256-token pages
+        # into a 64-token scratch (a step that touches every page)
+        npg = 512
+        pools = [torch.zeros((npg, 256 * wl.ROW_BYTES), dtype=torch.uint8, device=dev) for _ in range(4)]
+        scratch = torch.zeros((4 * npg, 64 * wl.ROW_BYTES), dtype=torch.uint8, device=dev)
+        pg = torch.arange(npg, dtype=torch.int32, device=dev)
+        us = burst(lambda i: smla.split_pages_64(pools[i % 4], pg, scratch), a.steps, a.warmup)
+        byts = 2 * npg * 256 * wl.ROW_BYTES + 4 * npg
+        extras["split_pages_512x256"] = {"us": round(float(us.mean()), 2),
+                                         "gbs": round(byts / (us.mean() * 1e-6) / 1e9, 1),
+                                         "hbm_frac": round(byts / (us.mean() * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"split pages 512 x 256: {us.mean():.2f} us")
+        del pools, scratch
     result["extras"] = extras
 
     # ---------------- oracle on the host cores, bounded sample ----------------

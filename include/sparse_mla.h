@@ -14,13 +14,15 @@
  *
  *   mla_kv_write_bf16, sparse_mla_attn_bf16;
  *
- * and two more around them:
+ * and three more around them:
  *
  *   mla_gather_upconvert  dequantises listed cache rows into a bf16 workspace
  *                         of 576-wide rows (the chunked-context reader's form);
  *   sparse_mla_merge      merges partial (out, lse) pairs of sparse_mla_attn
  *                         calls over disjoint shares of the top-k entries
- *                         (context-parallel decoding) by their log-sum-exp.
+ *                         (context-parallel decoding) by their log-sum-exp;
+ *   mla_split_pages_64    re-pages the touched 256-token pages of a pool into
+ *                         a zero-initialised scratch of 64-token pages.
  *
  * Common rules
  *   - Every pointer argument is a DEVICE pointer owned by the caller; the
@@ -214,6 +216,34 @@ int sparse_mla_attn_bf16(const void* q,
 int mla_gather_upconvert(const void* kv_cache, int64_t num_slots, int rope_dim,
                          const int64_t* slots, int64_t num_rows,
                          void* dst, int64_t dst_row_stride, hipStream_t stream);
+
+/*
+ * mla_split_pages_64 - re-page 256-token pages into a 64-token scratch.
+ *
+ * Follows sglang PR 39288, Root cause (2) and Modifications: a pool of
+ * 256-token pages is re-paged for a reader of 64-token pages by copying each
+ * source page a step references into four 64-token pages of a persistent
+ * scratch.  The scratch must be zero-filled by the caller when it is
+ * allocated (the pages' fix), so that its slot 0 is finite whether or not
+ * source page 0 is ever copied; this call copies and never clears.  For
+ * every listed page p with 0 <= p < num_src_pages (other entries are
+ * ignored; duplicates copy the same bytes twice) and k = 0..3:
+ *   dst + (4p + k) * dst_page_stride, 64 * row_bytes bytes
+ *     = src_pool + p * src_page_stride + k * 64 * row_bytes
+ * No other byte of dst is written (untouched pages and the padding past
+ * 64 * row_bytes in each dst page keep their contents).
+ *
+ * src_pool        uint8, num_src_pages pages of src_page_stride bytes
+ *                 (>= 256 * row_bytes, a multiple of 16), 16-byte aligned.
+ * pages           int32 [num_pages], the touched source pages.
+ * dst             uint8, >= 4 * num_src_pages pages of dst_page_stride bytes
+ *                 (>= 64 * row_bytes, a multiple of 16), 16-byte aligned.
+ * row_bytes       bytes per token row (656 for fp8_ds_mla), a multiple of 16.
+ */
+int mla_split_pages_64(const void* src_pool, int64_t num_src_pages, int64_t src_page_stride,
+                       const int32_t* pages, int64_t num_pages,
+                       void* dst, int64_t dst_page_stride, int row_bytes,
+                       hipStream_t stream);
 
 /*
  * sparse_mla_merge - combine partial attention results by their LSE.

@@ -16,5 +16,6 @@ Modules:
   merge     - log-sum-exp merge of partial (output, lse) results of disjoint
               shares of a row's top-k entries.
   gather    - listed cache rows dequantised into 576-wide bf16 rows.
+  pages     - re-paging of touched 256-token pages into a 64-token scratch.
 """
-from . import e4m3, writer, attention, merge, gather  # noqa: F401
+from . import e4m3, writer, attention, merge, gather, pages  # noqa: F401

@@ -10,6 +10,7 @@ and a missing or unloadable library raises.
          out=None, lse=None, workspace=None) -> (out, lse)
     merge(part_out, part_lse, out=None, lse=None) -> (out, lse)
     gather_upconvert(kv_cache, slots, rope_dim, out=None) -> out
+    split_pages_64(src_pool, pages, dst, row_bytes=656)
     kv_write_bf16(kv_c, k_pe, slot_mapping, kv_cache_bf16)
     attn_bf16(q, kv_cache_bf16, topk_idx, sm_scale, ...) -> (out, lse)
 """
@@ -46,6 +47,9 @@ _SIGS = {
     "mla_gather_upconvert": (ctypes.c_int, [
         ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
         ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]),
+    "mla_split_pages_64": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]),
     "sparse_mla_merge": (ctypes.c_int, [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
@@ -221,3 +225,18 @@ def attn_bf16(q, kv_cache, topk_idx, sm_scale: float, topk_capacity: int | None 
                                     ws_bytes, _stream(q))
     _check("sparse_mla_attn_bf16", rc)
     return out, lse
+
+
+def split_pages_64(src_pool, pages, dst, row_bytes: int = ROW_BYTES) -> None:
+    """Copy the listed 256-token pages of src_pool (uint8 [num_src_pages][>=256*row_bytes])
+    into 64-token pages of dst (uint8 [>=4*num_src_pages][>=64*row_bytes], zeroed
+    by the caller at allocation); pages int32 [n]."""
+    import torch
+    assert src_pool.dtype == torch.uint8 and src_pool.dim() == 2 and src_pool.stride(1) == 1
+    assert dst.dtype == torch.uint8 and dst.dim() == 2 and dst.stride(1) == 1
+    assert pages.dtype == torch.int32 and pages.dim() == 1 and pages.is_contiguous()
+    assert dst.shape[0] >= 4 * src_pool.shape[0]
+    rc = lib().mla_split_pages_64(src_pool.data_ptr(), src_pool.shape[0], src_pool.stride(0),
+                                  pages.data_ptr(), pages.shape[0], dst.data_ptr(), dst.stride(0),
+                                  int(row_bytes), _stream(src_pool))
+    _check("mla_split_pages_64", rc)

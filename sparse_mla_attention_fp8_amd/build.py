@@ -12,7 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsparse_mla.so")
-SOURCES = ["kv_write.hip", "attn.hip", "merge.hip", "gather.hip", "api.hip"]
+SOURCES = ["kv_write.hip", "attn.hip", "merge.hip", "gather.hip", "split_pages.hip", "api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

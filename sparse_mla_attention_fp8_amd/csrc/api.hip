@@ -199,6 +199,32 @@ int mla_gather_upconvert(const void* kv_cache, int64_t num_slots, int rope_dim,
   return SMLA_OK;
 }
 
+int mla_split_pages_64(const void* src_pool, int64_t num_src_pages, int64_t src_page_stride,
+                       const int32_t* pages, int64_t num_pages, void* dst, int64_t dst_page_stride,
+                       int row_bytes, hipStream_t stream) {
+  g_err[0] = '\0';
+  if (row_bytes < 16 || (row_bytes & 15))
+    return fail(SMLA_EINVAL, "mla_split_pages_64: row_bytes must be a positive multiple of 16, got %d", row_bytes);
+  if (num_src_pages < 1 || num_pages < 0)
+    return fail(SMLA_EINVAL, "mla_split_pages_64: need num_src_pages >= 1 and num_pages >= 0");
+  if (num_pages == 0) return SMLA_OK;
+  if (4 * num_pages > 0x7FFFFFFF) return fail(SMLA_EUNSUPPORTED, "mla_split_pages_64: too many pages");
+  if (src_pool == nullptr || pages == nullptr || dst == nullptr)
+    return fail(SMLA_EINVAL, "mla_split_pages_64: null pointer argument");
+  if (src_page_stride < 256 * (int64_t)row_bytes || (src_page_stride & 15))
+    return fail(SMLA_EINVAL, "mla_split_pages_64: src_page_stride must be >= 256 * row_bytes and a multiple of 16");
+  if (dst_page_stride < 64 * (int64_t)row_bytes || (dst_page_stride & 15))
+    return fail(SMLA_EINVAL, "mla_split_pages_64: dst_page_stride must be >= 64 * row_bytes and a multiple of 16");
+  if (!aligned16(src_pool) || !aligned16(dst) || (reinterpret_cast<uintptr_t>(pages) & 3u))
+    return fail(SMLA_EINVAL, "mla_split_pages_64: misaligned pointer");
+  hipError_t e = smla::launch_split_pages(static_cast<const uint8_t*>(src_pool), num_src_pages,
+                                          src_page_stride, pages, num_pages,
+                                          static_cast<uint8_t*>(dst), dst_page_stride, row_bytes, stream);
+  if (e != hipSuccess)
+    return fail(SMLA_ELAUNCH, "mla_split_pages_64: launch failed: %s", hipGetErrorString(e));
+  return SMLA_OK;
+}
+
 int sparse_mla_merge(const void* part_out, const float* part_lse, int P, int T, int H, void* out,
                      float* lse, hipStream_t stream) {
   g_err[0] = '\0';

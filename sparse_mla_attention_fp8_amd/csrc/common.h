@@ -48,6 +48,10 @@ hipError_t launch_gather_upconvert(const uint8_t* cache, int64_t num_slots, int 
                                    const int64_t* slots, int64_t n, uint16_t* dst,
                                    int64_t dst_stride, hipStream_t stream);
 
+hipError_t launch_split_pages(const uint8_t* src, int64_t num_src_pages, int64_t src_page_stride,
+                              const int32_t* pages, int64_t num_pages, uint8_t* dst,
+                              int64_t dst_page_stride, int row_bytes, hipStream_t stream);
+
 hipError_t launch_merge(const uint16_t* part_out, const float* part_lse, int P, int64_t rows,
                         uint16_t* out, float* lse, hipStream_t stream);
 

@@ -135,3 +135,20 @@ def test_gather_validation():
         assert rc == smla.SMLA_EINVAL, b
         assert L.smla_last_error().decode().startswith("mla_gather_upconvert")
     assert L.mla_gather_upconvert(*{**base, "num_rows": 0, "kv_cache": None}.values()) in (smla.SMLA_OK, smla.SMLA_EINVAL)
+
+
+def test_split_pages_validation():
+    L = smla.lib()
+    base = dict(src=FAKE, num_src=8, src_stride=256 * 656, pages=FAKE, num_pages=4,
+                dst=FAKE + 0x1000000, dst_stride=64 * 656, row_bytes=656, stream=None)
+    bad = [
+        dict(row_bytes=0), dict(row_bytes=650), dict(num_src=0), dict(num_pages=-1),
+        dict(src=None), dict(pages=None), dict(dst=None),
+        dict(src_stride=256 * 656 - 16), dict(dst_stride=64 * 656 - 16), dict(dst_stride=64 * 656 + 8),
+        dict(src=FAKE + 8), dict(pages=FAKE + 2),
+    ]
+    for b in bad:
+        a = {**base, **b}
+        rc = L.mla_split_pages_64(*a.values())
+        assert rc == smla.SMLA_EINVAL, b
+        assert L.smla_last_error().decode().startswith("mla_split_pages_64")
