@@ -160,19 +160,6 @@ __device__ __forceinline__ void split_e4m3(float x0, float x1, float x2, float x
   lo = (uint32_t)l;
 }
 
-// 4x4 byte transpose: in a_i byte j -> out b_j byte i
-__device__ __forceinline__ void tr4x4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,
-                                      uint32_t& b0, uint32_t& b1, uint32_t& b2, uint32_t& b3) {
-  const uint32_t t0 = __builtin_amdgcn_perm(a1, a0, 0x06020400u);
-  const uint32_t t1 = __builtin_amdgcn_perm(a1, a0, 0x07030501u);
-  const uint32_t t2 = __builtin_amdgcn_perm(a3, a2, 0x06020400u);
-  const uint32_t t3 = __builtin_amdgcn_perm(a3, a2, 0x07030501u);
-  b0 = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
-  b2 = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
-  b1 = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
-  b3 = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
-}
-
 // Max without NaN canonicalisation (operands are never signalling NaNs).
 __device__ __forceinline__ float fmax_nc(float a, float b) {
   float r;
