@@ -352,7 +352,30 @@ def main():
             log(f"{name}: {us.mean():.1f} us")
             if name == "rope_decode_T256":
                 gather_extra("gather_upconvert_rope_N65536", rot, 64)
+                # the RoPE decode curve: the first T rows of the same batch
+                for Tc in (1, 16, 64):
+                    sub = dict(c)
+                    sub["q"], sub["idx"] = c["q"][:Tc], c["idx"][:Tc]
+                    us, _, _ = time_attn(sub, rot, a.steps, a.warmup)
+                    b = gathered(sub, ROPE_ROW)
+                    extras[f"rope_decode_T{Tc}"] = {"us": round(float(us.mean()), 2),
+                                                   "gbs": round(b / (us.mean() * 1e-6) / 1e9, 1)}
+                    log(f"rope T={Tc}: {us.mean():.1f} us")
             del rot, cache
+        # sparse prefill of one causal sequence (rope 64): row t attends over
+        # tokens 0..t, so the rows are re-read from L2 and the kernel is not
+        # HBM-bound; reported as algorithmic score + P.V FLOP/s
+        for Tp in (65, 128, 1024):
+            cp = wl.config_prefill(Tp)
+            cache = build_cache(cp)
+            us, _, _ = time_attn(cp, [cache], a.steps, a.warmup)
+            nv = int((cp["idx"] >= 0).sum())
+            flops = 2.0 * 16 * (576 + 512) * nv
+            extras[f"prefill_T{Tp}"] = {"us": round(float(us.mean()), 2),
+                                        "tflops": round(flops / (us.mean() * 1e-6) / 1e12, 2),
+                                        "query_rows_per_us": round(Tp / us.mean(), 3)}
+            log(f"prefill T={Tp}: {us.mean():.1f} us")
+            del cache
         # BF16 KV cache: NoPE decode T=256 over rows of 512 bf16 values
         cb = wl.config_nope_decode(256)
         log("generating bf16_nope_decode_T256")

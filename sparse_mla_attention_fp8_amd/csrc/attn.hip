@@ -207,8 +207,14 @@ __device__ __forceinline__ long pack64(uint32_t lo, uint32_t hi) {
 // kPer - 1 (its loads all issued at once); an exclusive scan of the per-thread
 // counts (within a wavefront by shuffles, across wavefronts through LDS)
 // places them.  Two barriers in all.
+//
+// With share_splits > 0 the valid entries are dealt out instead: of the n
+// valid entries of [lo, hi), split `split` keeps positions [split * share,
+// (split + 1) * share) in buffer order, share = ceil(n / share_splits)
+// rounded up to whole 64-key chunks, so the splits of a row get equal work
+// wherever its padding sits.
 __device__ int compact_valid(const int32_t* __restrict__ idx, int lo, int hi, int64_t num_slots,
-                             int* list, int* wave_counts) {
+                             int* list, int* wave_counts, int split = 0, int share_splits = 0) {
   constexpr int kPer = (kMaxRange + kThreads - 1) / kThreads;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int k0 = lo + kPer * tid;
@@ -233,12 +239,22 @@ __device__ int compact_valid(const int32_t* __restrict__ idx, int lo, int hi, in
     total += c;
     base += w < wave ? c : 0;
   }
+  int w0 = 0, w1 = total;   // positions this split keeps
+  if (share_splits > 0) {
+    const int share = ((total + share_splits - 1) / share_splits + kKeys - 1) / kKeys * kKeys;
+    w0 = min(total, split * share);
+    w1 = min(total, w0 + share);
+  }
   int pos = base + x - cnt;
 #pragma unroll
-  for (int i = 0; i < kPer; ++i)
-    if (v[i] >= 0 && (int64_t)v[i] < num_slots) list[pos++] = v[i];
+  for (int i = 0; i < kPer; ++i) {
+    if (v[i] >= 0 && (int64_t)v[i] < num_slots) {
+      if (pos >= w0 && pos < w1) list[pos - w0] = v[i];
+      ++pos;
+    }
+  }
   __syncthreads();
-  return total;
+  return w1 - w0;
 }
 
 // SMALL: the cache spans less than 4 GiB, so row byte offsets fit 32 bits.
@@ -294,12 +310,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
     }
   }
 
-  const int lo_k = split * range;
-  const int hi_k = min(W, lo_k + range);
+  // range 0: every split scans the whole row and keeps its share of the valid entries
+  const int lo_k = range == 0 ? 0 : split * range;
+  const int hi_k = range == 0 ? W : min(W, lo_k + range);
   // (its barriers also publish the staged q: each wavefront's first wait for
   // its index loads covers its earlier q loads)
   const int n = __builtin_amdgcn_readfirstlane(
-      compact_valid(idx + (int64_t)t * idx_stride, lo_k, hi_k, num_slots, slot_list, wave_counts));
+      compact_valid(idx + (int64_t)t * idx_stride, lo_k, hi_k, num_slots, slot_list, wave_counts,
+                    split, range == 0 ? splits : 0));
   const int nch = (n + kKeys - 1) / kKeys;
 
   // q fragments of head n16: tile 2qh+u, dims 128(2qh+u) + 32g + 8k + [0, 8) -> qraw[4u + k]
@@ -755,10 +773,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
       if (i < 17 && h < nh && e < 64) dma16(qsrc + (int64_t)h * 1024 + 16 * e, lds_q + 1024u * (uint32_t)i);
     }
   }
-  const int lo_k = split * range;
-  const int hi_k = min(W, lo_k + range);
+  // range 0: every split scans the whole row and keeps its share of the valid entries
+  const int lo_k = range == 0 ? 0 : split * range;
+  const int hi_k = range == 0 ? W : min(W, lo_k + range);
   const int n = __builtin_amdgcn_readfirstlane(
-      compact_valid(idx + (int64_t)t * idx_stride, lo_k, hi_k, num_slots, slot_list, wave_counts));
+      compact_valid(idx + (int64_t)t * idx_stride, lo_k, hi_k, num_slots, slot_list, wave_counts,
+                    split, range == 0 ? splits : 0));
   const int nch = (n + kKeys - 1) / kKeys;
   // q fragments (B operand of the K-steps of half qh): dims 256qh + 32s + 8g + [0, 8)
   bf16x8 qf[8];
@@ -1081,8 +1101,18 @@ AttnPlan plan_attn(int T, int H, int W, int rope_dim) {
   p.head_groups = (H + kHeads - 1) / kHeads;
   const int units = T * p.head_groups;
   const int max_splits = (W + kKeys - 1) / kKeys;
-  int s = (kTargetBlocks + units - 1) / units;
-  s = s < 1 ? 1 : (s > max_splits ? max_splits : s);
+  // at most one round of workgroups (one per CU): a split count that spills
+  // a few workgroups into a second round doubles the launch
+  int s = units >= kTargetBlocks ? 1 : kTargetBlocks / units;
+  s = s > max_splits ? max_splits : s;
+  if (W <= kMaxRange) {
+    // the whole row fits one scan: every split deals the row's valid entries
+    // out evenly (range 0), so padding in the buffer costs no split any work
+    p.splits = s;
+    p.range = s > 1 ? 0 : W;
+    p.workspace = (s > 1) ? (size_t)T * s * H * (kLatent + 2) * sizeof(float) : 0;
+    return p;
+  }
   const int min_s = (W + kMaxRange - 1) / kMaxRange;
   if (s < min_s) s = min_s;
   int range = (W + s - 1) / s;

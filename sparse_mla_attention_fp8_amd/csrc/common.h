@@ -29,7 +29,8 @@ hipError_t launch_kv_write_bf16(const uint16_t* kv_c, int64_t kv_c_stride, const
 struct AttnPlan {
   int head_groups;   // ceil(H / 16)
   int splits;        // split-top-k count per (row, head group)
-  int range;         // top-k entries per split (multiple of the chunk size)
+  int range;         // top-k entries per split (multiple of the chunk size); 0: every split
+                     // scans the whole row and keeps an equal share of its valid entries
   size_t workspace;  // bytes of partial results (0 when splits == 1)
 };
 AttnPlan plan_attn(int T, int H, int topk_capacity, int rope_dim);

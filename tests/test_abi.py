@@ -152,3 +152,19 @@ def test_split_pages_validation():
         rc = L.mla_split_pages_64(*a.values())
         assert rc == smla.SMLA_EINVAL, b
         assert L.smla_last_error().decode().startswith("mla_split_pages_64")
+
+
+def test_plan_fits_one_round_of_workgroups():
+    """One workgroup runs per CU (256 on the chip), so the split count keeps a
+    launch to one round of workgroups: 65 rows take 3 splits (195 workgroups),
+    not 4 (260, where 4 would wait for a second round)."""
+    rec = 16 * 514 * 4
+    for T in range(1, 300):
+        ws = smla.workspace_size(T, 16, 2048, 64)
+        s = ws // (rec * T) if ws else 1
+        assert ws == 0 or ws == s * rec * T
+        assert s == 1 or s * T <= 256, (T, s)
+        assert s <= 32                               # no more splits than 64-key chunks
+    assert smla.workspace_size(65, 16, 2048, 64) == 3 * rec * 65
+    assert smla.workspace_size(64, 16, 2176, 0) == 4 * rec * 64
+    assert smla.workspace_size(257, 16, 2048, 64) == 0

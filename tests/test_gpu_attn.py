@@ -223,3 +223,20 @@ def test_cache_beyond_4_gib(rope_dim):
     ref_out, ref_lse = oracle_attn.sparse_mla_attn(q, host, idx, W, rope_dim, sm)
     del cache
     assert_parity(out, lse, ref_out, ref_lse, range(T))
+
+
+def test_buffer_wider_than_one_scan():
+    """A top-k buffer wider than one split's scan (3,000 > 2,304 entries): the
+    row is cut into fixed ranges instead of dealt out; valid entries and -1
+    padding interleaved across the whole width."""
+    cfg = wl.config_rope_decode(2, seed=700, num_slots=16384, ctx=(4000, 16000), W=3000)
+    rng = np.random.default_rng(7)
+    idx = np.full((2, 3000), -1, dtype=np.int32)
+    for t in range(2):
+        n = 2500 - 700 * t
+        pos = np.sort(rng.choice(3000, size=n, replace=False))
+        idx[t, pos] = rng.choice(np.arange(1, 16384), size=n, replace=False)
+    cache = build_cache(cfg)
+    out, lse = run_attn(cfg, cache, idx=idx)
+    ref_out, ref_lse = oracle_for(cfg, [0, 1], idx=idx)
+    assert_parity(out, lse, ref_out, ref_lse, [0, 1])
