@@ -11,9 +11,12 @@
 //
 // Mapping: one 64-lane wavefront per row.  Lane l owns latent values
 // 8l..8l+7 (one 16-byte load, one 8-byte store); the 16 lanes of a DPP row
-// form one 128-value tile, so the tile amax is a 16-lane reduction.  Lanes
-// 0..7 also move the 128-byte RoPE tail.  The kernel is HBM-bound: per kept
-// row it reads 1,152 B (1,024 without RoPE) and writes 656 B.
+// form one 128-value tile, so the tile amax is a 16-lane DPP reduction.
+// Lanes 0..7 also move the 128-byte RoPE tail.  Per kept row the kernel
+// reads 1,152 B (1,024 without RoPE) and writes 656 B; the quantiser's
+// arithmetic is kept short (one reciprocal per tile, three operations and a
+// hardware conversion per value) so that a wavefront's chain of slot load,
+// row load and store is not lengthened by it.
 #include "common.h"
 
 namespace smla {
@@ -41,6 +44,37 @@ __device__ __forceinline__ uint32_t e4m3_rne_satfinite(float v) {
   uint32_t code = (e << 3) + mant + (up & 1u); // a mantissa carry bumps the exponent
   code = code > 0x7Eu ? 0x7Eu : code;
   return sign | code;
+}
+
+
+// Four codes of x[0..3] / scale, by IEEE division and the integer encoder.
+__device__ __forceinline__ uint32_t encode4_exact(const float* x, float scale) {
+  uint32_t p = 0u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p |= e4m3_rne_satfinite(x[i] / scale) << (8 * i);
+  return p;
+}
+
+// DPP controls for a max over the 16 lanes of a row: swap neighbours, swap
+// pairs, mirror each half-row, mirror the row.
+constexpr int kQuadXor1 = 0xB1;       // quad_perm [1, 0, 3, 2]
+constexpr int kQuadXor2 = 0x4E;       // quad_perm [2, 3, 0, 1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+constexpr uint32_t kBits448 = 0x43E00000u;   // 448.0f
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_max(uint32_t v) {
+  return max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false));
+}
+
+// Four float32 values -> four e4m3 codes (byte i = value i) by the hardware
+// conversion (round to nearest even).  It agrees with e4m3_rne_satfinite for
+// every |v| <= 448; callers cap magnitudes at 448.
+__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
+  int p = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  p = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, p, true);
+  return (uint32_t)p;
 }
 
 __global__ __launch_bounds__(256) void kv_write_kernel(
@@ -71,22 +105,46 @@ __global__ __launch_bounds__(256) void kv_write_kernel(
     x[2 * i] = __uint_as_float(w[i] << 16);
     x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
   }
-  float amax = 0.0f;
+  // tile amax as an unsigned max of |x| bit patterns: the same order as the
+  // float max for numbers, and a NaN anywhere in the tile makes amax NaN
+  uint32_t am = 0u;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
-  // 16-lane (one tile) max reduction
-  amax = fmaxf(amax, __shfl_xor(amax, 8, 16));
-  amax = fmaxf(amax, __shfl_xor(amax, 4, 16));
-  amax = fmaxf(amax, __shfl_xor(amax, 2, 16));
-  amax = fmaxf(amax, __shfl_xor(amax, 1, 16));
+  for (int i = 0; i < 8; ++i) am = max(am, __float_as_uint(x[i]) & 0x7FFFFFFFu);
+  am = dpp_max<kQuadXor1>(am);
+  am = dpp_max<kQuadXor2>(am);
+  am = dpp_max<kRowHalfMirror>(am);
+  am = dpp_max<kRowMirror>(am);
+  const float amax = __uint_as_float(am);
 
   const float scale = amax / 448.0f;  // IEEE float32 division (correctly rounded)
   uint32_t lo = 0u, hi = 0u;
-  if (amax != 0.0f) {
+  if (scale >= 0x1p-60f && scale <= 3.4028234663852886e38f) {
+    // Fast path: the quotient x / scale from a reciprocal and one residual
+    // correction (Markstein), q1 = fma(fma(-q0, scale, x), r, q0) with
+    // r = fl32(1/scale) and q0 = fl32(x * r).  For a bf16 x and a float32
+    // scale this is the IEEE quotient fl32(x / scale): an exhaustive run over
+    // every float32 scale mantissa against every bf16 mantissa, in both
+    // relative binades, found no difference, and the scale bound keeps every
+    // intermediate normal wherever the quotient reaches the e4m3 grid.  The
+    // sign of zero is taken from x.  Magnitudes are capped at 448 (the largest
+    // code, to which every larger quotient saturates) before the hardware
+    // conversion, which rounds to nearest even and gives the codes of
+    // e4m3_rne_satfinite for every |v| <= 448.
+    const float r = 1.0f / scale;
+    float v[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lo |= e4m3_rne_satfinite(x[i] / scale) << (8 * i);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) hi |= e4m3_rne_satfinite(x[4 + i] / scale) << (8 * i);
+    for (int i = 0; i < 8; ++i) {
+      const float q0 = __fmul_rn(x[i], r);
+      const float q1 = __builtin_fmaf(__builtin_fmaf(-q0, scale, x[i]), r, q0);
+      const uint32_t mag = min(__float_as_uint(q1) & 0x7FFFFFFFu, kBits448);
+      v[i] = __uint_as_float(mag | (__float_as_uint(x[i]) & 0x80000000u));
+    }
+    lo = pack4_e4m3(v[0], v[1], v[2], v[3]);
+    hi = pack4_e4m3(v[4], v[5], v[6], v[7]);
+  } else if (amax != 0.0f) {
+    // tiny, huge or non-finite tiles: divide and encode exactly
+    lo = encode4_exact(x, scale);
+    hi = encode4_exact(x + 4, scale);
   }
   *reinterpret_cast<uint2*>(dst + lane * 8) = make_uint2(lo, hi);
   if ((lane & 15) == 0)

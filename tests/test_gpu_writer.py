@@ -112,3 +112,68 @@ def test_out_of_range_slots_are_dropped():
     want = cfg["cache"].copy()
     oracle_writer.kv_write(want, lat, None, slots)
     assert np.array_equal(got, want)
+
+
+def _tiles_below(amax_bits: int) -> np.ndarray:
+    """Tiles of 128 bf16 values: element 0 is the tile maximum (amax_bits, so
+    every tile has the same scale) and the rest run through every bf16 value
+    of smaller magnitude, both signs."""
+    bits = np.arange(1 << 15, dtype=np.uint32)
+    vals = bits[bits < amax_bits]
+    vals = np.concatenate([vals, vals | 0x8000]).astype(np.uint16)
+    n_tiles = (vals.size + 126) // 127
+    tiles = np.zeros((n_tiles, 128), dtype=np.uint16)
+    flat = np.zeros(n_tiles * 127, dtype=np.uint16)
+    flat[: vals.size] = vals
+    tiles[:, 1:] = flat.reshape(n_tiles, 127)
+    tiles[:, 0] = amax_bits
+    return tiles
+
+
+def test_every_bf16_value_at_many_scales():
+    """For 24 tile maxima (so 24 scales whose reciprocal is inexact), every
+    bf16 value below the maximum in magnitude is quantised: each quotient
+    x / scale, its e4m3 rounding and every tie that the scale produces are
+    compared byte for byte with the oracle."""
+    rng = np.random.default_rng(11)
+    exps = rng.integers(-60, 60, size=24)
+    mants = rng.integers(0, 128, size=24)
+    mants[:4] = [0, 1, 0x3F, 0x7F]
+    tiles = np.concatenate([_tiles_below(int(((e + 127) << 7) | m)) for e, m in zip(exps, mants)])
+    pad = (-tiles.shape[0]) % 4
+    if pad:
+        tiles = np.concatenate([tiles, tiles[:pad]])
+    lat = tiles.reshape(-1, 512)
+    n = lat.shape[0]
+    cfg = dict(cache=np.zeros((n + 1, 656), dtype=np.uint8), latent=lat, rope=None,
+               slots=np.arange(1, n + 1, dtype=np.int64))
+    got = _run(cfg)
+    want = cfg["cache"].copy()
+    oracle_writer.kv_write(want, lat, None, cfg["slots"])
+    assert np.array_equal(got, want)
+
+
+def test_nan_input_in_a_kept_row():
+    """A NaN in a kept row is not sanitised: its tile stores a NaN scale and NaN
+    codes (0x7F or 0xFF) only, as the oracle's amax = NaN gives; the row's
+    other tiles are exact."""
+    rng = np.random.default_rng(12)
+    lat = wl.normal_bf16(rng, (4, 512))
+    lat[1, 200] = 0x7FC0                     # NaN in tile 1 of row 1
+    lat[2, 5] = 0xFFC0                       # negative NaN in tile 0 of row 2
+    cfg = dict(cache=np.zeros((5, 656), dtype=np.uint8), latent=lat, rope=None,
+               slots=np.arange(1, 5, dtype=np.int64))
+    got = _run(cfg)
+    want = cfg["cache"].copy()
+    oracle_writer.kv_write(want, lat, None, cfg["slots"])
+    for row, tile in ((2, 1), (3, 0)):
+        codes = got[row, 128 * tile:128 * (tile + 1)]
+        assert np.all((codes & 0x7F) == 0x7F)
+        assert np.isnan(got[row, 512 + 4 * tile:516 + 4 * tile].view("<f4")[0])
+        assert np.all(np.isnan(oracle_writer.encode_rows(lat[row - 1:row], None)[0, 512:528]
+                               .view("<f4")[tile:tile + 1]))
+        keep = np.ones(656, dtype=bool)
+        keep[128 * tile:128 * (tile + 1)] = False
+        keep[512 + 4 * tile:516 + 4 * tile] = False
+        assert np.array_equal(got[row][keep], want[row][keep])
+    assert np.array_equal(got[[0, 1, 4]], want[[0, 1, 4]])
