@@ -394,6 +394,25 @@ def main():
                                            "gbs": round(b / (us.mean() * 1e-6) / 1e9, 1),
                                            "hbm_frac": round(b / (us.mean() * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
         log(f"bf16_nope_decode_T256: {us.mean():.1f} us")
+        del rotb, cacheb
+        # BF16 KV cache: RoPE decode T=256 over rows of 512 + 64 bf16 values
+        cr = wl.config_rope_decode(256)
+        log("generating bf16_rope_decode_T256")
+        cacher = torch.zeros((cr["num_slots"], 576), dtype=torch.bfloat16, device=dev)
+        smla.kv_write_bf16(bf16_dev(cr["latent"]), bf16_dev(cr["rope"]),
+                           torch.from_numpy(cr["slots"]).to(dev), cacher)
+        nrr = max(2, int(np.ceil(600e6 / (cacher.numel() * 2))))
+        rotr = [cacher] + [cacher.clone() for _ in range(nrr - 1)]
+        qr_ = bf16_dev(cr["q"])
+        idxr = torch.from_numpy(cr["idx"]).to(dev)
+        us = burst(lambda i: smla.attn_bf16(qr_, rotr[i % nrr], idxr, cr["sm_scale"], out=ob, lse=lb),
+                   a.steps, a.warmup)
+        b = gathered(cr, 1152)
+        extras["bf16_rope_decode_T256"] = {"us": round(float(us.mean()), 2),
+                                           "gbs": round(b / (us.mean() * 1e-6) / 1e9, 1),
+                                           "hbm_frac": round(b / (us.mean() * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"bf16_rope_decode_T256: {us.mean():.1f} us")
+        del rotr, cacher
         wb = wl.config_writer(N=8192, rope_dim=0)
         wcache = torch.zeros((wb["cache"].shape[0], 512), dtype=torch.bfloat16, device=dev)
         wlat = bf16_dev(wb["latent"])
@@ -405,7 +424,7 @@ def main():
                                             "gbs": round((written * (1024 + 1024 + 8) + (8192 - written) * 8)
                                                          / (us.mean() * 1e-6) / 1e9, 1)}
         log(f"writer bf16 rope0: {us.mean():.2f} us")
-        del rotb, cacheb, wcache
+        del wcache
         # LSE merge of 8 partial results (context-parallel decode over 8 owners),
         # T=256, H=16; inputs rotated over copies larger than the Infinity Cache
         Pm, Tm, Hm = 8, 256, 16

@@ -175,12 +175,12 @@ int mla_kv_write_bf16(const void* kv_c, int64_t kv_c_row_stride,
  * sparse_mla_attn_bf16 - sparse MLA attention over a BF16 KV cache.
  *
  * The computation of sparse_mla_attn with K_j[e] = the bf16 value stored at
- * kv_cache[j][e] (no dequantisation).  This build supports NoPE rows only:
- * rope_dim 0, kv_cache bf16 [num_slots][512]; rope_dim 64 returns
- * SMLA_EUNSUPPORTED (a 1,152-byte row does not fit the kernel's two LDS
- * stages).  All other arguments, the padding rules, the workspace (same size
- * as sparse_mla_attn_workspace_size) and the error behaviour are those of
- * sparse_mla_attn.
+ * kv_cache[j][e] (no dequantisation): kv_cache is bf16 [num_slots][512 +
+ * rope_dim] as mla_kv_write_bf16 writes it, 16-byte aligned, and q is bf16
+ * [T][H][512 + rope_dim]; scores run over all 512 + rope_dim dimensions, the
+ * output over the 512 latent ones.  All other arguments, the padding rules,
+ * the workspace (same size as sparse_mla_attn_workspace_size) and the error
+ * behaviour are those of sparse_mla_attn.
  */
 int sparse_mla_attn_bf16(const void* q,
                          const void* kv_cache, int64_t num_slots,

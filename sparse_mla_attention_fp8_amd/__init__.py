@@ -203,11 +203,14 @@ def kv_write_bf16(kv_c, k_pe, slot_mapping, kv_cache) -> None:
 
 def attn_bf16(q, kv_cache, topk_idx, sm_scale: float, topk_capacity: int | None = None,
               out=None, lse=None, workspace=None, want_lse: bool = True):
-    """Sparse MLA attention over the BF16 cache kv_cache bf16 [num_slots][512]
-    (NoPE).  q bf16 [T][H][512]; topk_idx int32 [T][>=W]."""
+    """Sparse MLA attention over the BF16 cache kv_cache bf16 [num_slots][512 + rope_dim];
+    q bf16 [T][H][512 + rope_dim] (rope_dim 0 or 64, read from q's width);
+    topk_idx int32 [T][>=W]."""
     import torch
-    assert q.dtype == torch.bfloat16 and q.dim() == 3 and q.is_contiguous() and q.shape[2] == LATENT
-    assert kv_cache.dtype == torch.bfloat16 and kv_cache.is_contiguous() and kv_cache.shape[-1] == LATENT
+    assert q.dtype == torch.bfloat16 and q.dim() == 3 and q.is_contiguous()
+    rope_dim = q.shape[2] - LATENT
+    assert rope_dim in (0, 64)
+    assert kv_cache.dtype == torch.bfloat16 and kv_cache.is_contiguous() and kv_cache.shape[-1] == q.shape[2]
     assert topk_idx.dtype == torch.int32 and topk_idx.dim() == 2 and topk_idx.stride(1) == 1
     T, H, _ = q.shape
     W = topk_idx.shape[1] if topk_capacity is None else int(topk_capacity)
@@ -215,12 +218,12 @@ def attn_bf16(q, kv_cache, topk_idx, sm_scale: float, topk_capacity: int | None 
         out = torch.empty((T, H, LATENT), dtype=torch.bfloat16, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
-    need = workspace_size(T, H, W, 0)
+    need = workspace_size(T, H, W, rope_dim)
     if need and (workspace is None or workspace.numel() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    rc = lib().sparse_mla_attn_bf16(q.data_ptr(), kv_cache.data_ptr(), kv_cache.numel() // LATENT,
-                                    topk_idx.data_ptr(), topk_idx.stride(0), W, T, H, 0,
+    rc = lib().sparse_mla_attn_bf16(q.data_ptr(), kv_cache.data_ptr(), kv_cache.numel() // q.shape[2],
+                                    topk_idx.data_ptr(), topk_idx.stride(0), W, T, H, rope_dim,
                                     float(sm_scale), out.data_ptr(), _ptr(lse), _ptr(workspace),
                                     ws_bytes, _stream(q))
     _check("sparse_mla_attn_bf16", rc)

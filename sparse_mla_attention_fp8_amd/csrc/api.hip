@@ -142,8 +142,6 @@ int sparse_mla_attn_bf16(const void* q, const void* kv_cache, int64_t num_slots,
   g_err[0] = '\0';
   if (rope_dim != 0 && rope_dim != 64)
     return fail(SMLA_EINVAL, "sparse_mla_attn_bf16: rope_dim must be 0 or 64, got %d", rope_dim);
-  if (rope_dim == 64)
-    return fail(SMLA_EUNSUPPORTED, "sparse_mla_attn_bf16: only NoPE rows (rope_dim 0) are supported");
   if (T < 1 || H < 1 || H > SMLA_MAX_HEADS)
     return fail(SMLA_EINVAL, "sparse_mla_attn_bf16: need T >= 1 and 1 <= H <= %d (T=%d, H=%d)",
                 SMLA_MAX_HEADS, T, H);
@@ -167,7 +165,7 @@ int sparse_mla_attn_bf16(const void* q, const void* kv_cache, int64_t num_slots,
   }
   hipError_t e = smla::launch_attn_bf16(static_cast<const uint16_t*>(q),
                                         static_cast<const uint16_t*>(kv_cache), num_slots, topk_idx,
-                                        idx_row_stride, topk_capacity, T, H, sm_scale,
+                                        idx_row_stride, topk_capacity, T, H, rope_dim, sm_scale,
                                         static_cast<uint16_t*>(out), lse, workspace, plan, stream);
   if (e != hipSuccess)
     return fail(SMLA_ELAUNCH, "sparse_mla_attn_bf16: launch failed: %s", hipGetErrorString(e));

@@ -716,12 +716,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// BF16 KV cache: rows are bf16 [num_slots][512] (1,024 bytes, NoPE), the cache
-// form of sglang PR 47013, Speed Tests (its timed writer stores 512 bf16
-// values per row, and its end-to-end runs use a BF16 KV cache).  The same
-// pipeline as attn_mfma_kernel, with:
-//   * rows staged at a 1,040-byte LDS pitch (one idle lane per 65 of the
-//     gather lays out a 16-byte pad), so rows start 4 banks apart;
+// BF16 KV cache: rows are bf16 [num_slots][512 + ROPE] (1,024 or 1,152
+// bytes), the cache form of sglang PR 47013, Speed Tests (its timed writer
+// stores 512 bf16 values per row, and its end-to-end runs use a BF16 KV
+// cache).  The same pipeline as attn_mfma_kernel, with:
+//   * the 512 latent values of each row staged at a 1,040-byte LDS pitch (one
+//     idle lane per 65 of the gather lays out a 16-byte pad), so rows start 4
+//     banks apart;
+//   * with RoPE, the 64 RoPE values of a chunk's keys loaded by the QK^T
+//     wavefronts straight into registers (16 bytes per lane: key n16, dims
+//     32qh + 8g of the RoPE part), issued right after the chunk's gather and
+//     covered by the same waits, two register sets deep; two 66,560-byte
+//     stages of whole 1,152-byte rows would not fit beside the index list;
 //   * QK^T on v_mfma_f32_16x16x32_bf16 (8 K-steps of 32 dims per 256-dim
 //     half), q used as is;
 //   * P.V on v_mfma_f32_16x16x32_bf16 with P rounded once to bf16 and V^T
@@ -735,7 +741,7 @@ constexpr int kB16Instr = kKeys * (kB16Pitch / 16) / 64;   // 65 x 1-KB loads pe
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 
-template <bool SMALL>
+template <int ROPE, bool SMALL>
 __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ cache, int64_t num_slots,
     const int32_t* __restrict__ idx, int64_t idx_stride, int W, int H, float sm_scale_log2,
@@ -759,20 +765,26 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
   const int head = hg * kHeads + n16;
   const bool hvalid = head < H;
   const uint8_t* cache8 = reinterpret_cast<const uint8_t*>(cache);
+  constexpr int D = kLatent + ROPE;           // q and cache row width (elements)
+  constexpr uint32_t RS = 2u * D;             // cache row bytes
 
   // ---- q of the group's heads -> LDS at the same padded pitch -------------
   {
     const int nh = min(kHeads, H - hg * kHeads);
-    const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(q + ((int64_t)t * H + hg * kHeads) * kLatent);
+    const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(q + ((int64_t)t * H + hg * kHeads) * D);
     const uint32_t lds_q = lds_addr(stages);
 #pragma unroll
     for (int j = 0; j < (17 + kWaves - 1) / kWaves; ++j) {
       const int i = wave + kWaves * j;           // 16 rows x 65 segments = 1,040 -> 17 loads
       const int f = 64 * i + lane;
       const int h = f / 65, e = f - h * 65;
-      if (i < 17 && h < nh && e < 64) dma16(qsrc + (int64_t)h * 1024 + 16 * e, lds_q + 1024u * (uint32_t)i);
+      if (i < 17 && h < nh && e < 64) dma16(qsrc + (int64_t)h * RS + 16 * e, lds_q + 1024u * (uint32_t)i);
     }
   }
+  // RoPE k-step qh of head n16: dims 512 + 32qh + 8g + [0, 8), from global memory
+  uint4 qpe_raw = make_uint4(0, 0, 0, 0);
+  if (ROPE && hvalid)
+    qpe_raw = *reinterpret_cast<const uint4*>(q + ((int64_t)t * H + head) * D + kLatent + 32 * qh + 8 * g);
   // range 0: every split scans the whole row and keeps its share of the valid entries
   const int lo_k = range == 0 ? 0 : split * range;
   const int hi_k = range == 0 ? W : min(W, lo_k + range);
@@ -791,6 +803,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
       qf[s] = __builtin_bit_cast(bf16x8, v);
     }
   }
+  const bf16x8 qpe = __builtin_bit_cast(bf16x8, qpe_raw);
 
   // ---- gather geometry: load i = wave + 8j covers LDS segments 64i + lane;
   // segment f is row f / 65, piece f % 65 (piece 64 is the pad, not loaded)
@@ -806,30 +819,42 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
     seg_off[j] = (f - seg_row[j] * 65) * 16;                          // 1,024 = the pad
   }
   int slot[CNT0];
+  const int pe_row = key_row(qb, n16);         // this lane's key for the RoPE loads
+  int pe_slot = 0;
   auto fetch_slots = [&](int c) {
     const int base = c * kKeys;
     const int nv = min(kKeys, n - base);
     if (nv == kKeys) {
 #pragma unroll
       for (int j = 0; j < CNT0; ++j) slot[j] = slot_list[base + seg_row[j]];
+      if (ROPE) pe_slot = slot_list[base + pe_row];
     } else {
 #pragma unroll
       for (int j = 0; j < CNT0; ++j) slot[j] = slot_list[base + (seg_row[j] < nv ? seg_row[j] : 0)];
+      if (ROPE) pe_slot = slot_list[base + (pe_row < nv ? pe_row : 0)];
     }
   };
-  auto issue = [&](uint32_t stage) {
+  // the chunk's latent rows -> LDS, then (RoPE) this lane's 16 RoPE bytes ->
+  // pe: one more load per wavefront and chunk, behind the chunk's gather
+  auto issue = [&](uint32_t stage, uint4& pe) {
 #pragma unroll
     for (int j = 0; j < CNT0; ++j) {
       if (j < my_cnt && seg_off[j] < 1024) {
         const uint32_t lds = stage + 1024u * (uint32_t)(wave + kWaves * j);
         if (SMALL) {
-          dma16_sbase(cache8, (uint32_t)slot[j] * 1024u + (uint32_t)seg_off[j], lds);
+          dma16_sbase(cache8, (uint32_t)slot[j] * RS + (uint32_t)seg_off[j], lds);
         } else {
-          dma16(cache8 + (int64_t)slot[j] * 1024 + seg_off[j], lds);
+          dma16(cache8 + (int64_t)slot[j] * RS + seg_off[j], lds);
         }
       }
     }
+    if (ROPE) {
+      const uint8_t* src = cache8 + (SMALL ? (int64_t)((uint32_t)pe_slot * RS) : (int64_t)pe_slot * RS) +
+                           2 * (kLatent + 32 * qh + 8 * g);
+      pe = *reinterpret_cast<const uint4*>(src);
+    }
   };
+  uint4 pe_buf[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};   // RoPE rows of chunks c, c+1 (by c & 1)
 
   float m_run = -1e30f;
   float l_run = 0.0f;
@@ -865,14 +890,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
     for (int s = 0; s < 8; ++s) o.a[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(krow + 64 * s));
     return o;
   };
-  auto qk_mfma = [&](const QkLoad& k) {
+  auto qk_mfma = [&](const QkLoad& k, const uint4& pe) {
     const f4 z4 = f4{0.0f, 0.0f, 0.0f, 0.0f};
-    f4 e = z4, d = z4;   // two chains of four K-steps
+    f4 e = z4, d = z4;   // two chains of four K-steps (plus the RoPE K-step qh)
 #pragma unroll
     for (int s = 0; s < 8; s += 2) {
       e = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k.a[s], qf[s], e, 0, 0, 0);
       d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k.a[s + 1], qf[s + 1], d, 0, 0, 0);
     }
+    if (ROPE) e = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pe), qpe, e, 0, 0, 0);
     return e + d;
   };
   auto qk_finish = [&](const f4 acc, int c) {
@@ -887,16 +913,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
   for (int c = 0; c < kB16NST; ++c)
     if (c < nch) {
       fetch_slots(c);
-      issue(lds0 + (uint32_t)(c * kB16Stage));
+      issue(lds0 + (uint32_t)(c * kB16Stage), pe_buf[c]);
     }
   if (kB16NST < nch) fetch_slots(kB16NST);
   if (nch > 0) {
-    if (nch > 1) { if (big) vm_barrier<CNT0>(); else vm_barrier<CNT1>(); }
+    // chunk 0 landed: at most chunk 1's loads (its gather, and its RoPE load) outstanding
+    constexpr int kPe = ROPE ? 1 : 0;
+    if (nch > 1) { if (big) vm_barrier<CNT0 + kPe>(); else vm_barrier<CNT1 + kPe>(); }
     else vm_barrier<0>();
-    qk_finish(qk_mfma(qk_load(stages)), 0);
+    qk_finish(qk_mfma(qk_load(stages), pe_buf[0]), 0);
     read_pv(stages, va[0]);
   }
-  auto step = [&](const int c, const bf16x8* vc, bf16x8* vn) {
+  // pc holds chunk c's RoPE loads (reused for chunk c+2), pn chunk c+1's
+  auto step = [&](const int c, const bf16x8* vc, bf16x8* vn, uint4& pc, const uint4& pnx) {
     // chunk c+1 landed (nothing issued after it), chunk c's scores visible,
     // chunk c's stage free
     vm_barrier<0>();
@@ -906,7 +935,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
 #pragma unroll
       for (int h = 0; h < 2; ++h) u[bb][h] = xs[c & 1][2 * ps + bb][h][lane];
     const int cur = c % kB16NST;
-    if (c + kB16NST < nch) issue(lds0 + (uint32_t)(cur * kB16Stage));
+    if (c + kB16NST < nch) issue(lds0 + (uint32_t)(cur * kB16Stage), pc);
     const uint8_t* nstg = stages + ((c + 1) % kB16NST) * kB16Stage;
     const QkLoad nk = qk_load(nstg);
     read_pv(nstg, vn);
@@ -947,15 +976,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
     bf16x8 pb;
 #pragma unroll
     for (int e = 0; e < 8; ++e) pb[e] = (__bf16)pn[e];
-    const f4 nq = qk_mfma(nk);
+    const f4 nq = qk_mfma(nk, pnx);
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc) oacc[cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vc[cc], pb, oacc[cc], 0, 0, 0);
     if (c + 1 < nch) qk_finish(nq, c + 1);
   };
   for (int c = 0; c < nch; c += 2) {
-    step(c, va[0], va[1]);
+    step(c, va[0], va[1], pe_buf[0], pe_buf[1]);
     if (c + 1 >= nch) break;
-    step(c + 1, va[1], va[0]);
+    step(c + 1, va[1], va[0], pe_buf[1], pe_buf[0]);
   }
 
   // ---- combine the two key halves, then write ------------------------------
@@ -1157,7 +1186,7 @@ hipError_t launch_attn(const uint16_t* q, const uint8_t* cache, int64_t num_slot
 
 hipError_t launch_attn_bf16(const uint16_t* q, const uint16_t* cache, int64_t num_slots,
                             const int32_t* idx, int64_t idx_stride, int W, int T, int H,
-                            float sm_scale, uint16_t* out, float* lse, void* workspace,
+                            int rope_dim, float sm_scale, uint16_t* out, float* lse, void* workspace,
                             const AttnPlan& plan, hipStream_t stream) {
   float* part_o = nullptr;
   float* part_ml = nullptr;
@@ -1167,13 +1196,18 @@ hipError_t launch_attn_bf16(const uint16_t* q, const uint16_t* cache, int64_t nu
   }
   const int64_t blocks = (int64_t)plan.splits * T * plan.head_groups;
   const float sl2 = sm_scale * kLog2e;
-  const bool small = num_slots <= (int64_t)(0xFFFFFFFFull / 1024);   // row byte offsets fit 32 bits
+  // row byte offsets fit 32 bits
+  const bool small = num_slots <= (int64_t)(0xFFFFFFFFull / (2 * (kLatent + rope_dim)));
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, q, cache, num_slots,
                        idx, idx_stride, W, H, sl2, plan.range, plan.splits, plan.head_groups, out,
                        lse, part_o, part_ml);
   };
-  if (small) go(attn_bf16_kernel<true>); else go(attn_bf16_kernel<false>);
+  if (rope_dim == 64) {
+    if (small) go(attn_bf16_kernel<64, true>); else go(attn_bf16_kernel<64, false>);
+  } else {
+    if (small) go(attn_bf16_kernel<0, true>); else go(attn_bf16_kernel<0, false>);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.splits == 1) return e;
   hipLaunchKernelGGL(attn_merge_kernel, dim3(T * H), dim3(64 * kMergeWaves), 0, stream, part_o, part_ml,

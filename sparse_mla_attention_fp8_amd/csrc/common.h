@@ -42,7 +42,7 @@ hipError_t launch_attn(const uint16_t* q, const uint8_t* cache, int64_t num_slot
 
 hipError_t launch_attn_bf16(const uint16_t* q, const uint16_t* cache, int64_t num_slots,
                             const int32_t* idx, int64_t idx_stride, int W, int T, int H,
-                            float sm_scale, uint16_t* out, float* lse, void* workspace,
+                            int rope_dim, float sm_scale, uint16_t* out, float* lse, void* workspace,
                             const AttnPlan& plan, hipStream_t stream);
 
 hipError_t launch_gather_upconvert(const uint8_t* cache, int64_t num_slots, int rope_dim,

@@ -1,8 +1,8 @@
 """HIP BF16-cache writer and attention vs the float64 oracle: the writer byte
-for byte (slot rule, NaN padding rows), attention on NoPE decode rows with
-splits and a merge, padding anywhere, empty rows and out-of-range entries, a
-NaN row in the reserved slot, head counts, the full-size decode batch
-(sampled rows) and a cache beyond 4 GiB."""
+for byte (slot rule, NaN padding rows), attention on NoPE and RoPE decode rows
+with splits and a merge, padding anywhere, empty rows and out-of-range
+entries, a NaN row in the reserved slot, head counts, prefill rows, the
+full-size decode batches (sampled rows) and caches beyond 4 GiB."""
 import numpy as np
 import pytest
 import torch
@@ -22,23 +22,27 @@ def _bits(t):
 
 def _build(cfg, check=True):
     """BF16 cache written by the HIP writer (checked against the oracle), slot 0 = NaN row."""
-    cache = torch.zeros((cfg["num_slots"], 512), dtype=torch.bfloat16, device=DEV)
-    smla.kv_write_bf16(bf16_dev(cfg["latent"]), None, torch.from_numpy(cfg["slots"]).to(DEV), cache)
+    width = 512 + cfg["rope_dim"]
+    rope = cfg["rope"] if cfg["rope_dim"] else None
+    cache = torch.zeros((cfg["num_slots"], width), dtype=torch.bfloat16, device=DEV)
+    smla.kv_write_bf16(bf16_dev(cfg["latent"]), None if rope is None else bf16_dev(rope),
+                       torch.from_numpy(cfg["slots"]).to(DEV), cache)
     torch.cuda.synchronize()
     if check:
-        host = np.zeros((cfg["num_slots"], 512), dtype=np.uint16)
-        oracle_writer.kv_write_bf16(host, cfg["latent"], None, cfg["slots"])
+        host = np.zeros((cfg["num_slots"], width), dtype=np.uint16)
+        oracle_writer.kv_write_bf16(host, cfg["latent"], rope, cfg["slots"])
         assert np.array_equal(_bits(cache), host)
-    cache[0] = torch.from_numpy(np.full(512, 0x7FC0, dtype=np.uint16).view(np.int16)).view(torch.bfloat16).to(DEV)
+    cache[0] = torch.from_numpy(np.full(width, 0x7FC0, dtype=np.uint16).view(np.int16)).view(torch.bfloat16).to(DEV)
     return cache
 
 
 def _oracle(cfg, cache, idx, rows):
     need = idx[list(rows)].ravel()
     need = np.unique(need[(need >= 0) & (need < cfg["num_slots"])])
-    host = np.zeros((cfg["num_slots"], 512), dtype=np.uint16)
+    host = np.zeros((cfg["num_slots"], cache.shape[1]), dtype=np.uint16)
     host[need] = _bits(cache[torch.from_numpy(need).to(DEV)])
-    return oracle_attn.sparse_mla_attn_bf16(cfg["q"], host, idx, idx.shape[1], 0, cfg["sm_scale"], rows=list(rows))
+    return oracle_attn.sparse_mla_attn_bf16(cfg["q"], host, idx, idx.shape[1], cache.shape[1] - 512,
+                                            cfg["sm_scale"], rows=list(rows))
 
 
 def _run(cfg, cache, idx, W=None):
@@ -77,8 +81,32 @@ def test_nope_decode_small_cache(T):
     assert_parity(out, lse, ref_out, ref_lse, range(T))
 
 
-def test_padding_anywhere_empty_rows_and_out_of_range():
-    cfg = wl.config_nope_decode(8, seed=410, num_slots=4096, ctx=(256, 4096))
+@pytest.mark.parametrize("T", [1, 16, 64])
+def test_rope_decode_small_cache(T):
+    """RoPE rows (512 + 64 bf16 values, 576-d scores), W = 2048."""
+    print(f"bf16 rope decode T={T}", flush=True)
+    cfg = wl.config_rope_decode(T, seed=430 + T, num_slots=32768, ctx=(2048, 30000))
+    cache = _build(cfg)
+    out, lse = _run(cfg, cache, cfg["idx"])
+    ref_out, ref_lse = _oracle(cfg, cache, cfg["idx"], range(T))
+    assert_parity(out, lse, ref_out, ref_lse, range(T))
+
+
+@pytest.mark.parametrize("T", [65, 130])
+def test_rope_prefill_rows(T):
+    """Causal prefill rows over RoPE rows: row t lists tokens <= t, then -1."""
+    print(f"bf16 rope prefill T={T}", flush=True)
+    cfg = wl.config_prefill(T, num_slots=8192)
+    cache = _build(cfg)
+    out, lse = _run(cfg, cache, cfg["idx"])
+    ref_out, ref_lse = _oracle(cfg, cache, cfg["idx"], range(T))
+    assert_parity(out, lse, ref_out, ref_lse, range(T))
+
+
+@pytest.mark.parametrize("rope", [False, True])
+def test_padding_anywhere_empty_rows_and_out_of_range(rope):
+    cfg = (wl.config_rope_decode(8, seed=411, num_slots=4096, ctx=(256, 4096), W=2176) if rope else
+           wl.config_nope_decode(8, seed=410, num_slots=4096, ctx=(256, 4096)))
     cache = _build(cfg)
     rng = np.random.default_rng(7)
     idx = cfg["idx"].copy()
@@ -94,18 +122,22 @@ def test_padding_anywhere_empty_rows_and_out_of_range():
 
 
 @pytest.mark.parametrize("H", [4, 16, 40])
-def test_head_counts(H):
-    cfg = wl.config_nope_decode(5, seed=420 + H, num_slots=4096, ctx=(256, 4096), H=H)
+@pytest.mark.parametrize("rope", [False, True])
+def test_head_counts(H, rope):
+    cfg = (wl.config_rope_decode(5, seed=425 + H, num_slots=4096, ctx=(256, 4096), H=H) if rope else
+           wl.config_nope_decode(5, seed=420 + H, num_slots=4096, ctx=(256, 4096), H=H))
     cache = _build(cfg)
     out, lse = _run(cfg, cache, cfg["idx"])
     ref_out, ref_lse = _oracle(cfg, cache, cfg["idx"], range(5))
     assert_parity(out, lse, ref_out, ref_lse, range(5))
 
 
-def test_full_size_decode_sampled():
-    """The full NoPE decode batch (T = 256, 131,072-slot cache, W = 2176),
-    in the launch configuration the bench times; 24 rows checked."""
-    cfg = wl.config_nope_decode(256)
+@pytest.mark.parametrize("rope", [False, True])
+def test_full_size_decode_sampled(rope):
+    """The full decode batches (T = 256: NoPE, 131,072-slot cache, W = 2176;
+    RoPE, 262,144-slot cache, W = 2048), in the launch configuration the
+    bench times; 24 rows checked."""
+    cfg = wl.config_rope_decode(256) if rope else wl.config_nope_decode(256)
     cache = _build(cfg, check=False)
     out, lse = _run(cfg, cache, cfg["idx"])
     rows = list(range(0, 256, 11))
@@ -113,28 +145,25 @@ def test_full_size_decode_sampled():
     assert_parity(out, lse, ref_out, ref_lse, rows)
 
 
-def test_cache_beyond_4_gib():
-    num_slots = 4_500_000                                # 4.6 GB of 1,024-byte rows
-    rng = np.random.default_rng(9)
-    cache = torch.zeros((num_slots, 512), dtype=torch.bfloat16, device=DEV)
+@pytest.mark.parametrize("rope_dim", [0, 64])
+def test_cache_beyond_4_gib(rope_dim):
+    """4,500,000 rows of 1,024 or 1,152 bytes (4.6 / 5.2 GB): row byte offsets
+    past 2^32 take the kernel's 64-bit address path."""
+    num_slots = 4_500_000
+    width = 512 + rope_dim
+    assert num_slots * 2 * width > 2**32
+    rng = np.random.default_rng(9 + rope_dim)
+    cache = torch.zeros((num_slots, width), dtype=torch.bfloat16, device=DEV)
     T, W = 4, 512
     idx = np.stack([np.concatenate([rng.integers(4_200_000, num_slots, size=300),
                                     rng.integers(1, 1000, size=W - 300)]) for _ in range(T)]).astype(np.int32)
     uniq = np.unique(idx)
     lat = wl.normal_bf16(rng, (uniq.size, 512))
-    smla.kv_write_bf16(bf16_dev(lat), None, torch.from_numpy(uniq.astype(np.int64)).to(DEV), cache)
-    q = wl.normal_bf16(rng, (T, 16, 512))
-    cfg = dict(num_slots=num_slots, q=q, sm_scale=float(1 / np.sqrt(512)))
+    pe = wl.normal_bf16(rng, (uniq.size, 64)) if rope_dim else None
+    smla.kv_write_bf16(bf16_dev(lat), None if pe is None else bf16_dev(pe),
+                       torch.from_numpy(uniq.astype(np.int64)).to(DEV), cache)
+    q = wl.normal_bf16(rng, (T, 16, width))
+    cfg = dict(num_slots=num_slots, q=q, sm_scale=float(1 / np.sqrt(width)))
     out, lse = _run(cfg, cache, idx)
     ref_out, ref_lse = _oracle(cfg, cache, idx, range(T))
     assert_parity(out, lse, ref_out, ref_lse, range(T))
-
-
-def test_rope_rows_are_reported_unsupported():
-    q = torch.zeros((1, 16, 576), dtype=torch.bfloat16, device=DEV)
-    cache = torch.zeros((8, 576), dtype=torch.bfloat16, device=DEV)
-    idx = torch.zeros((1, 4), dtype=torch.int32, device=DEV)
-    out = torch.empty((1, 16, 512), dtype=torch.bfloat16, device=DEV)
-    rc = smla.lib().sparse_mla_attn_bf16(q.data_ptr(), cache.data_ptr(), 8, idx.data_ptr(), 4, 4, 1, 16, 64,
-                                         0.05, out.data_ptr(), None, None, 0, None)
-    assert rc == smla.SMLA_EUNSUPPORTED
