@@ -1122,6 +1122,81 @@ __global__ __launch_bounds__(64 * kMergeWaves) void attn_merge_kernel(const floa
   if (lse != nullptr && lane == 0) lse[th] = (Lt > 0.0f) ? (M + __log2f(Lt)) * kLn2 : -INFINITY;
 }
 
+
+// The same combination for few splits (at most kMergeSmallMax): one wavefront
+// per (row, head), four per 256-thread block; lane l owns dims 8l..8l+7.  The
+// splits are taken eight at a time with a running maximum, every load of a
+// group issued before any is used, so up to eight splits cost one memory round
+// trip and no LDS.  The eight-wavefront kernel above wins only when there are
+// many splits to spread over its wavefronts.
+constexpr int kMergeSmallMax = 16;
+constexpr int kMergeSmallRows = 4;
+
+__global__ __launch_bounds__(64 * kMergeSmallRows) void attn_merge_small_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_ml, int splits, int H, int rows,
+    uint16_t* __restrict__ out, float* __restrict__ lse) {
+  const int lane = threadIdx.x & 63;
+  const int th = blockIdx.x * kMergeSmallRows + (threadIdx.x >> 6);   // t * H + h
+  if (th >= rows) return;
+  const int t = th / H, hh = th % H;
+  const float* ml = part_ml + 2 * ((int64_t)t * splits * H + hh);   // split s at ml[2 * s * H]
+  const float* po_base = part_o + ((int64_t)t * splits * H + hh) * kLatent + 8 * lane;
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+  float M = -INFINITY, L = 0.0f;
+  for (int s0 = 0; s0 < splits; s0 += 8) {
+    float ms[8], ls[8];
+    float4 a[8], c[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int s = s0 + j;
+      const bool in = s < splits;
+      ms[j] = in ? ml[2 * (int64_t)s * H] : -INFINITY;
+      ls[j] = in ? ml[2 * (int64_t)s * H + 1] : 0.0f;
+      const float4* src = reinterpret_cast<const float4*>(po_base + (int64_t)s * H * kLatent);
+      a[j] = in ? src[0] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      c[j] = in ? src[1] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+    float mg = M;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mg = fmaxf(mg, ms[j]);
+    const float f = __builtin_amdgcn_exp2f(M - mg);   // 0 on the first group
+    L *= f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] *= f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float w = __builtin_amdgcn_exp2f(ms[j] - mg);   // 0 for the padding j
+      L += w * ls[j];
+      acc[0] += w * a[j].x; acc[1] += w * a[j].y; acc[2] += w * a[j].z; acc[3] += w * a[j].w;
+      acc[4] += w * c[j].x; acc[5] += w * c[j].y; acc[6] += w * c[j].z; acc[7] += w * c[j].w;
+    }
+    M = mg;
+  }
+  const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
+  uint32_t pk[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    pk[i] = (uint32_t)f32_to_bf16_rne(acc[2 * i] * inv) | ((uint32_t)f32_to_bf16_rne(acc[2 * i + 1] * inv) << 16);
+  *reinterpret_cast<uint4*>(out + (int64_t)th * kLatent + 8 * lane) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+  if (lse != nullptr && lane == 0) lse[th] = (L > 0.0f) ? (M + __log2f(L)) * kLn2 : -INFINITY;
+}
+
+// Launches the merge that suits the split count.
+hipError_t launch_merge(const float* part_o, const float* part_ml, int splits, int T, int H,
+                        uint16_t* out, float* lse, hipStream_t stream) {
+  const int rows = T * H;
+  if (splits <= kMergeSmallMax) {
+    hipLaunchKernelGGL(attn_merge_small_kernel, dim3((rows + kMergeSmallRows - 1) / kMergeSmallRows),
+                       dim3(64 * kMergeSmallRows), 0, stream, part_o, part_ml, splits, H, rows, out, lse);
+  } else {
+    hipLaunchKernelGGL(attn_merge_kernel, dim3(rows), dim3(64 * kMergeWaves), 0, stream, part_o, part_ml,
+                       splits, H, out, lse);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 AttnPlan plan_attn(int T, int H, int W, int rope_dim) {
@@ -1179,9 +1254,7 @@ hipError_t launch_attn(const uint16_t* q, const uint8_t* cache, int64_t num_slot
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.splits == 1) return e;
-  hipLaunchKernelGGL(attn_merge_kernel, dim3(T * H), dim3(64 * kMergeWaves), 0, stream, part_o, part_ml,
-                     plan.splits, H, out, lse);
-  return hipGetLastError();
+  return launch_merge(part_o, part_ml, plan.splits, T, H, out, lse, stream);
 }
 
 hipError_t launch_attn_bf16(const uint16_t* q, const uint16_t* cache, int64_t num_slots,
@@ -1210,9 +1283,7 @@ hipError_t launch_attn_bf16(const uint16_t* q, const uint16_t* cache, int64_t nu
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.splits == 1) return e;
-  hipLaunchKernelGGL(attn_merge_kernel, dim3(T * H), dim3(64 * kMergeWaves), 0, stream, part_o, part_ml,
-                     plan.splits, H, out, lse);
-  return hipGetLastError();
+  return launch_merge(part_o, part_ml, plan.splits, T, H, out, lse, stream);
 }
 
 }  // namespace smla
