@@ -286,7 +286,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
   const int split = b % splits;
   b /= splits;
   const int hg = b % head_groups;
-  const int t = b / head_groups;
+  // rows last-first: in a causal prefill later rows list more entries, so the
+  // longest workgroups are dispatched first and fewer of them trail at the end
+  // (rows of a decode batch cost the same either way)
+  const int t = (int)(gridDim.x / (unsigned)(splits * head_groups)) - 1 - b / head_groups;
 
   // ---- q of the group's heads -> LDS (one copy per workgroup, issued before
   // the index scan), rows padded by 16 bytes so the fragment reads below fall
@@ -761,7 +764,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
   const int split = b % splits;
   b /= splits;
   const int hg = b % head_groups;
-  const int t = b / head_groups;
+  // rows last-first: in a causal prefill later rows list more entries, so the
+  // longest workgroups are dispatched first and fewer of them trail at the end
+  // (rows of a decode batch cost the same either way)
+  const int t = (int)(gridDim.x / (unsigned)(splits * head_groups)) - 1 - b / head_groups;
   const int head = hg * kHeads + n16;
   const bool hvalid = head < H;
   const uint8_t* cache8 = reinterpret_cast<const uint8_t*>(cache);
