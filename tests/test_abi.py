@@ -4,6 +4,8 @@ import ctypes
 import glob
 import os
 import re
+import subprocess
+import sys
 
 import pytest
 
@@ -168,3 +170,21 @@ def test_plan_fits_one_round_of_workgroups():
     assert smla.workspace_size(65, 16, 2048, 64) == 3 * rec * 65
     assert smla.workspace_size(64, 16, 2176, 0) == 4 * rec * 64
     assert smla.workspace_size(257, 16, 2048, 64) == 0
+
+
+def test_missing_library_raises(monkeypatch):
+    """No fallback: without the built library every entry point raises."""
+    monkeypatch.setattr(smla, "_lib", None)
+    monkeypatch.setattr(smla, "LIB_PATH", os.path.join(os.path.dirname(smla.LIB_PATH), "absent.so"))
+    with pytest.raises(ImportError):
+        smla.lib()
+    with pytest.raises(ImportError):
+        smla.workspace_size(1, 16, 2048, 64)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The benchmark measures one GPU; asking for more exits with a message."""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=60)
+    assert r.returncode == 2 and "one GPU" in r.stderr
