@@ -203,41 +203,47 @@ __device__ __forceinline__ long pack64(uint32_t lo, uint32_t hi) {
 }
 
 // Compacts the valid entries of idx[lo, hi) into list[] in buffer order and
-// returns their count.  Thread i takes entries lo + kPer*i .. lo + kPer*i +
-// kPer - 1 (its loads all issued at once); an exclusive scan of the per-thread
-// counts (within a wavefront by shuffles, across wavefronts through LDS)
-// places them.  Two barriers in all.
+// returns their count.  In round r thread i takes entry lo + 512r + i, so each
+// wavefront's loads are contiguous and all five rounds are issued at once; a
+// wavefront ballot per round gives its count, the counts of every (round,
+// wavefront) meet in LDS in buffer order, and each lane places its entry at its
+// group's base plus the valid lanes below it (mbcnt).  Two barriers in all.
 //
 // With share_splits > 0 the valid entries are dealt out instead: of the n
 // valid entries of [lo, hi), split `split` keeps positions [split * share,
 // (split + 1) * share) in buffer order, share = ceil(n / share_splits)
 // rounded up to whole 64-key chunks, so the splits of a row get equal work
 // wherever its padding sits.
+constexpr int kScanRounds = (kMaxRange + kThreads - 1) / kThreads;
+
 __device__ int compact_valid(const int32_t* __restrict__ idx, int lo, int hi, int64_t num_slots,
-                             int* list, int* wave_counts, int split = 0, int share_splits = 0) {
-  constexpr int kPer = (kMaxRange + kThreads - 1) / kThreads;
+                             int* list, int* group_counts /* [kScanRounds * kWaves] */,
+                             int split = 0, int share_splits = 0) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int k0 = lo + kPer * tid;
-  int v[kPer];
+  int v[kScanRounds];
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) v[i] = k0 + i < hi ? idx[k0 + i] : -1;
-  int cnt = 0;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) cnt += (v[i] >= 0 && (int64_t)v[i] < num_slots) ? 1 : 0;
-  int x = cnt;   // inclusive prefix within the wavefront
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off);
-    if (lane >= off) x += y;
+  for (int r = 0; r < kScanRounds; ++r) {
+    const int k = lo + kThreads * r + tid;
+    v[r] = k < hi ? idx[k] : -1;
   }
-  if (lane == 63) wave_counts[wave] = x;
-  __syncthreads();
-  int base = 0, total = 0;
+  uint64_t m[kScanRounds];
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const int c = wave_counts[w];
-    total += c;
-    base += w < wave ? c : 0;
+  for (int r = 0; r < kScanRounds; ++r) m[r] = __ballot(v[r] >= 0 && (int64_t)v[r] < num_slots);
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < kScanRounds; ++r) group_counts[r * kWaves + wave] = __popcll(m[r]);
+  }
+  __syncthreads();
+  int base[kScanRounds];
+  int total = 0;
+#pragma unroll
+  for (int r = 0; r < kScanRounds; ++r) {
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const int c = group_counts[r * kWaves + w];
+      if (w == wave) base[r] = total;
+      total += c;
+    }
   }
   int w0 = 0, w1 = total;   // positions this split keeps
   if (share_splits > 0) {
@@ -245,12 +251,12 @@ __device__ int compact_valid(const int32_t* __restrict__ idx, int lo, int hi, in
     w0 = min(total, split * share);
     w1 = min(total, w0 + share);
   }
-  int pos = base + x - cnt;
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    if (v[i] >= 0 && (int64_t)v[i] < num_slots) {
-      if (pos >= w0 && pos < w1) list[pos - w0] = v[i];
-      ++pos;
+  for (int r = 0; r < kScanRounds; ++r) {
+    if ((m[r] >> lane) & 1ull) {
+      const int pos = base[r] + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m[r] >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)m[r], 0u));
+      if (pos >= w0 && pos < w1) list[pos - w0] = v[r];
     }
   }
   __syncthreads();
@@ -270,7 +276,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
   __shared__ __align__(16) uint8_t stages[G::NST * G::STAGE];   // ring of 64-row stages
   __shared__ int slot_list[kMaxRange];
   __shared__ __align__(16) float4 xs[2][4][2][64];   // [chunk & 1][block][dim half][lane]: partial scores, keys 4g+r
-  __shared__ int wave_counts[kWaves];
+  __shared__ int wave_counts[kScanRounds * kWaves];
 
   const int tid = threadIdx.x, lane = tid & 63;
   // wave-uniform values are made visibly uniform so that every barrier sits on
@@ -753,7 +759,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
   __shared__ __align__(16) uint8_t stages[kB16NST * kB16Stage];
   __shared__ int slot_list[kMaxRange];
   __shared__ __align__(16) float4 xs[2][4][2][64];
-  __shared__ int wave_counts[kWaves];
+  __shared__ int wave_counts[kScanRounds * kWaves];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
