@@ -21,7 +21,7 @@ int fail(int code, const char* fmt, ...) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-constexpr int kMaxRows = 65535;  // query rows per call (grid y extent)
+constexpr int kMaxRows = 65535;  // query rows per call: every launch grid stays below 2^31 workgroups
 
 }  // namespace
 
@@ -38,6 +38,7 @@ int mla_kv_write(const void* kv_c, int64_t kv_c_row_stride, const void* k_pe,
   if (num_rows < 0) return fail(SMLA_EINVAL, "mla_kv_write: num_rows < 0");
   if (num_slots < 1) return fail(SMLA_EINVAL, "mla_kv_write: num_slots must be >= 1");
   if (num_rows == 0) return SMLA_OK;
+  if ((num_rows + 3) / 4 > 0x7FFFFFFF) return fail(SMLA_EUNSUPPORTED, "mla_kv_write: too many rows");
   if (kv_c == nullptr || slot_mapping == nullptr || kv_cache == nullptr)
     return fail(SMLA_EINVAL, "mla_kv_write: null pointer argument");
   if (rope_dim == 64 && k_pe == nullptr)
@@ -69,6 +70,7 @@ int mla_kv_write_bf16(const void* kv_c, int64_t kv_c_row_stride, const void* k_p
   if (num_rows < 0) return fail(SMLA_EINVAL, "mla_kv_write_bf16: num_rows < 0");
   if (num_slots < 1) return fail(SMLA_EINVAL, "mla_kv_write_bf16: num_slots must be >= 1");
   if (num_rows == 0) return SMLA_OK;
+  if ((num_rows + 3) / 4 > 0x7FFFFFFF) return fail(SMLA_EUNSUPPORTED, "mla_kv_write_bf16: too many rows");
   if (kv_c == nullptr || slot_mapping == nullptr || kv_cache == nullptr)
     return fail(SMLA_EINVAL, "mla_kv_write_bf16: null pointer argument");
   if (rope_dim == 64 && k_pe == nullptr)

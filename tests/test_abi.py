@@ -62,6 +62,9 @@ def test_kv_write_validation():
         assert L.smla_last_error().decode().startswith("mla_kv_write")
     # zero rows is a no-op that launches nothing
     assert L.mla_kv_write(*{**base, "num_rows": 0}.values()) == smla.SMLA_OK
+    # a row count whose grid would not fit is refused before any launch
+    assert L.mla_kv_write(*{**base, "num_rows": 1 << 34}.values()) == smla.SMLA_EUNSUPPORTED
+    assert L.mla_kv_write_bf16(*{**base, "num_rows": 1 << 34}.values()) == smla.SMLA_EUNSUPPORTED
 
 
 def test_attn_validation():
