@@ -13,7 +13,7 @@
 // The dequantised value is rounded once to fp32 (the precision of the stored
 // scale), then to bf16, both to nearest even.
 //
-// Mapping: one 64-lane wavefront per 4 rows, whose loads are all issued
+// Mapping: one 64-lane wavefront per 2 rows, whose loads are all issued
 // before any is used.  Lane l owns latent values 8l..8l+7 of a row: one 8-byte
 // code load, its tile's scale, one 16-byte store.  Lanes 0..7 also move the
 // 128-byte RoPE tail (or store its zeros).  HBM-bound: per row it reads
@@ -24,7 +24,7 @@ namespace smla {
 namespace {
 
 constexpr int kGatherWaves = 4;          // wavefronts per 256-thread block
-constexpr int kRowsPerWave = 4;          // rows per wavefront, loaded together
+constexpr int kRowsPerWave = 2;          // rows per wavefront, loaded together
 typedef float f2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
