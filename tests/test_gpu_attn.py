@@ -251,3 +251,21 @@ def test_buffer_wider_than_one_scan():
     out, lse = run_attn(cfg, cache, idx=idx)
     ref_out, ref_lse = oracle_for(cfg, [0, 1], idx=idx)
     assert_parity(out, lse, ref_out, ref_lse, [0, 1])
+
+
+def test_maximum_row_count():
+    """65,535 query rows (the largest call): one workgroup per row; sampled
+    rows against the oracle, every row finite."""
+    print("max rows", flush=True)
+    base = _tiny()
+    rng = np.random.default_rng(21)
+    T, W = 65535, 8
+    idx = np.full((T, W), -1, dtype=np.int32)
+    idx[:, :5] = rng.integers(1, base["num_slots"], size=(T, 5))
+    cfg = dict(base, T=T, H=1, W=W, q=wl.normal_bf16(rng, (T, 1, 576)), idx=idx)
+    cache = build_cache(cfg)
+    out, lse = run_attn(cfg, cache)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    rows = np.concatenate([np.arange(0, 64), rng.choice(T, size=64, replace=False), np.arange(T - 64, T)])
+    ref_out, ref_lse = oracle_for(cfg, rows)
+    assert_parity(out, lse, ref_out, ref_lse, rows)
