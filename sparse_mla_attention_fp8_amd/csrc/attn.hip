@@ -7,9 +7,10 @@
 // exact zero weight, so NaN-coded bytes in slot 0 cannot reach the output.
 //
 // Work decomposition.  One 512-thread workgroup (8 wavefronts, two per SIMD)
-// per (split, query row, group of 16 heads).  A split owns a contiguous range
-// of the row's top-k buffer; the workgroup compacts the valid entries of its
-// range into LDS and walks them in chunks of 64 keys:
+// per (split, query row, group of 16 heads).  A split owns an equal share of
+// the row's valid entries (or, for a buffer wider than one scan, a fixed range
+// of it); the workgroup compacts its entries into LDS in buffer order and
+// walks them in chunks of 64 keys:
 //
 //   gather  Each chunk's 64 rows (656 B, or the 528 B a NoPE reader needs)
 //           are copied HBM -> LDS with direct-to-LDS 16-byte loads, once per
@@ -45,7 +46,8 @@
 //
 // The key halves merge through LDS at the end.  With one split the workgroup
 // writes the bf16 output and LSE; with several it writes (O unnormalised fp32,
-// m, l) partials that attn_merge combines.  m is kept in log2 units throughout.
+// m, l) partials that a merge kernel combines (attn_merge_small_kernel up to
+// 16 splits, attn_merge_kernel beyond).  m is kept in log2 units throughout.
 #include "common.h"
 
 namespace smla {
