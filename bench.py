@@ -308,22 +308,23 @@ def main():
 
     if not a.no_extras:
         # writer standalone: 8,192 rows, a quarter aimed at slot 0 with NaN inputs
-        for rope_dim in (64, 0):
-            wc = wl.config_writer(N=8192, rope_dim=rope_dim)
-            cache = torch.from_numpy(wc["cache"]).to(dev)
-            lat = bf16_dev(wc["latent"])
-            rope = bf16_dev(wc["rope"]) if rope_dim else None
-            sl = torch.from_numpy(wc["slots"]).to(dev)
-            us = burst(lambda i: smla.kv_write(lat, rope, sl, cache), a.steps, a.warmup)
-            written = int((wc["slots"] > 0).sum())
-            byts = written * ((1024 + (128 if rope_dim else 0)) + 656 + 8) + (8192 - written) * 8
-            extras[f"writer_8192_rope{rope_dim}"] = {
-                "us": round(float(us.mean()), 3),
-                "rows_per_us": round(8192 / us.mean(), 1),
-                "written_rows_per_us": round(written / us.mean(), 1),
-                "gbs": round(byts / (us.mean() * 1e-6) / 1e9, 1),
-            }
-            log(f"writer rope{rope_dim}: {us.mean():.2f} us")
+        for N in (8192, 1024):
+            for rope_dim in (64, 0):
+                wc = wl.config_writer(N=N, rope_dim=rope_dim)
+                cache = torch.from_numpy(wc["cache"]).to(dev)
+                lat = bf16_dev(wc["latent"])
+                rope = bf16_dev(wc["rope"]) if rope_dim else None
+                sl = torch.from_numpy(wc["slots"]).to(dev)
+                us = burst(lambda i: smla.kv_write(lat, rope, sl, cache), a.steps, a.warmup)
+                written = int((wc["slots"] > 0).sum())
+                byts = written * ((1024 + (128 if rope_dim else 0)) + 656 + 8) + (N - written) * 8
+                extras[f"writer_{N}_rope{rope_dim}"] = {
+                    "us": round(float(us.mean()), 3),
+                    "rows_per_us": round(N / us.mean(), 1),
+                    "written_rows_per_us": round(written / us.mean(), 1),
+                    "gbs": round(byts / (us.mean() * 1e-6) / 1e9, 1),
+                }
+                log(f"writer {N} rope{rope_dim}: {us.mean():.2f} us")
         # NoPE decode curve
         cfgc = wl.config_nope_decode(64)
         cachec = build_cache(cfgc)
