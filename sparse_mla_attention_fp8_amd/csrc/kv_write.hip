@@ -83,7 +83,8 @@ __global__ __launch_bounds__(256) void kv_write_kernel(
     const int64_t* __restrict__ slot_mapping, int64_t num_rows,
     uint8_t* __restrict__ cache, int64_t num_slots) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  // wave-uniform row, so the slot id comes through one scalar load
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (row >= num_rows) return;
   const int64_t slot = slot_mapping[row];
   if (slot <= 0 || slot >= num_slots) return;  // dropped: inputs never read
@@ -160,7 +161,8 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void kv_write_bf16_kernel(
     int64_t k_pe_stride, int rope_dim, const int64_t* __restrict__ slot_mapping, int64_t num_rows,
     uint16_t* __restrict__ cache, int64_t num_slots) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  // wave-uniform row, so the slot id comes through one scalar load
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (row >= num_rows) return;
   const int64_t slot = slot_mapping[row];
   if (slot <= 0 || slot >= num_slots) return;   // dropped before any input load
