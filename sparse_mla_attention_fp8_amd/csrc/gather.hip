@@ -38,7 +38,8 @@ __global__ __launch_bounds__(64 * kGatherWaves) void gather_upconvert_kernel(
     const uint8_t* __restrict__ cache, int64_t num_slots, int rope_dim,
     const int64_t* __restrict__ slots, int64_t n, uint16_t* __restrict__ dst, int64_t dst_stride) {
   const int lane = threadIdx.x & 63;
-  const int64_t i0 = ((int64_t)blockIdx.x * kGatherWaves + (threadIdx.x >> 6)) * kRowsPerWave;
+  // wave-uniform rows, so the slot ids come through scalar loads
+  const int64_t i0 = ((int64_t)blockIdx.x * kGatherWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * kRowsPerWave;
   if (i0 >= n) return;
   // all of this wavefront's loads first, so kRowsPerWave rows are in flight at once
   bool ok[kRowsPerWave];
