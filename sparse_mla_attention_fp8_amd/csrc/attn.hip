@@ -1150,7 +1150,7 @@ __global__ __launch_bounds__(64 * kMergeSmallRows) void attn_merge_small_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml, int splits, int H, int rows,
     uint16_t* __restrict__ out, float* __restrict__ lse) {
   const int lane = threadIdx.x & 63;
-  const int th = blockIdx.x * kMergeSmallRows + (threadIdx.x >> 6);   // t * H + h
+  const int th = blockIdx.x * kMergeSmallRows + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // t * H + h (wave-uniform)
   if (th >= rows) return;
   const int t = th / H, hh = th % H;
   const float* ml = part_ml + 2 * ((int64_t)t * splits * H + hh);   // split s at ml[2 * s * H]

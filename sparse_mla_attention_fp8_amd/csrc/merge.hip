@@ -42,7 +42,7 @@ __global__ __launch_bounds__(64 * kMergeRowsPerBlock) void merge_partials_kernel
     const uint16_t* __restrict__ part_out, const float* __restrict__ part_lse, int P,
     int64_t rows, uint16_t* __restrict__ out, float* __restrict__ lse) {
   const int lane = threadIdx.x & 63;
-  const int64_t r = (int64_t)blockIdx.x * kMergeRowsPerBlock + (threadIdx.x >> 6);   // t * H + h
+  const int64_t r = (int64_t)blockIdx.x * kMergeRowsPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // t * H + h (wave-uniform)
   if (r >= rows) return;
   const uint4* src = reinterpret_cast<const uint4*>(part_out + r * kLatent) + lane;
   const int64_t pstride = rows * (kLatent / 8);   // uint4 units between parts
