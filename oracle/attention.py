@@ -8,8 +8,9 @@ What is computed (the plain definition; sglang PR 47013 Motivation, sglang PR
   A1  For query row t the valid entries are idx[t][k], k < W, with
       0 <= idx < num_slots; any negative entry (the pages use -1) is padding,
       wherever it sits in the row.  W is the buffer's capacity (vLLM PR 55277,
-      Purpose (2): the kernel is handed the physical top-k width and bounds the
-      active length by the -1 padding).  Duplicated entries count once each.
+      Purpose (2): the width passed in is that of the physical buffer, and the
+      -1 entries, not a length argument, mark where it is unused).  Duplicated
+      entries count once each.
   A2  Each referenced row is dequantised: K[e] = E4M3(code[e]) * scale[e // 128]
       for e < 512, and K[512 + r] = bf16 RoPE value r when rope_dim = 64.
   A3  s_j = sm_scale * sum_d q[t,h,d] * K_j[d] over d < 512 + rope_dim.

@@ -9,8 +9,8 @@ for the four 128-element tiles of the 512-wide latent means one 4-byte float32
 scale per tile; the RoPE part is 64 bf16 values (128 bytes).
 
 Writes aimed at the reserved padding slot 0 are dropped and their inputs are
-never looked at (sglang PR 47013, Summary and Modifications: the writers skip
-the slot reserved for padding rows, whose inputs are undefined).  Out-of-range
+never looked at (sglang PR 47013, Summary and Modifications: padding rows of a
+batch point at the reserved slot, and what they carry is undefined).  Out-of-range
 slots (< 0 or >= num_slots) are dropped as well; that part is this
 implementation's reading, not something the pages state.
 

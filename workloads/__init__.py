@@ -7,8 +7,8 @@ the HIP path can both be fed from it without sharing any of the computation.
 Shapes follow the workloads the source pages describe:
 
 * sglang PR 47013 (zero-RoPE writer skips slot 0), Speed Tests: writer calls of
-  1,024 and 8,192 bf16 rows of 512 values, a quarter of them padding rows
-  aimed at slot 0; decode at 16 heads, d_v 512, top-k 2048, 1-256 tokens.
+  1,024 and 8,192 bf16 rows of 512 values, with one row in four a padding row
+  for slot 0; decode at 16 heads, d_v 512, top-k 2048, 1-256 tokens.
 * sglang PR 39288 (SM120 page-split scratch), Root cause and kernel-harness
   table: 64-token pages, H=16, -1 padding, slot 0 holding 0xFF, random or zero
   bytes, prefill T=65 / decode T=64 boundary.
@@ -197,8 +197,8 @@ def config_disjoint(T: int = 64, seed: int = 60, num_slots: int = 262144,
 def config_writer(N: int = 8192, rope_dim: int = ROPE, seed: int = 50,
                   num_slots: int = 131072, pad_frac: float = 0.25,
                   shuffle: bool = False) -> dict:
-    """Standalone writer call: N rows, the trailing pad_frac of them padding rows
-    aimed at slot 0 whose inputs are bf16 NaN; the rest go to distinct random
+    """Standalone writer call: N rows, the trailing pad_frac of which are padding
+    rows for slot 0 with bf16 NaN inputs; the rest go to distinct random
     slots >= 1.  The cache starts as 0xA5 except slot 0, which is zero."""
     rng = np.random.default_rng(seed)
     n_pad = int(round(N * pad_frac))
