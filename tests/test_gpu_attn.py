@@ -269,3 +269,29 @@ def test_maximum_row_count():
     rows = np.concatenate([np.arange(0, 64), rng.choice(T, size=64, replace=False), np.arange(T - 64, T)])
     ref_out, ref_lse = oracle_for(cfg, rows)
     assert_parity(out, lse, ref_out, ref_lse, rows)
+
+
+@pytest.mark.parametrize("T,poison", [(65, "ff"), (65, "7f"), (64, "ff"), (64, "random")])
+def test_page_harness_shapes_have_no_nan_rows(T, poison):
+    """The kernel-harness shapes of sglang PR 39288, Root cause (one 64-page
+    cache, H = 16, T = 65 prefill / 64 decode rows, most of them padded with
+    -1, slot 0 holding NaN-coded or random bytes): where a reader that clamps
+    -1 to slot 0 turns every padded row into NaN, this kernel gives no NaN
+    and matches the oracle, bit for bit the same output as with slot 0 zeroed."""
+    print(f"harness T={T} slot0={poison}", flush=True)
+    rng = np.random.default_rng(900 + T)
+    num_slots, W = 64 * 64, 44 if T == 65 else 43
+    latent, rope, slots = wl.cache_rows(rng, num_slots, 64)
+    idx, _ = wl.prefill_topk(rng, T, W, num_slots)
+    assert int((idx < 0).any(axis=1).sum()) >= W - 1
+    cfg = dict(num_slots=num_slots, rope_dim=64, T=T, H=16, W=W, latent=latent, rope=rope,
+               slots=slots, q=wl.normal_bf16(rng, (T, 16, 576)), idx=idx,
+               sm_scale=float(1 / np.sqrt(576)), slot0=wl.slot0_bytes(rng, poison))
+    cache = build_cache(cfg)
+    out, lse = run_attn(cfg, cache)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    ref_out, ref_lse = oracle_for(cfg, range(T))
+    assert_parity(out, lse, ref_out, ref_lse, range(T))
+    cache[0] = 0
+    out0, lse0 = run_attn(cfg, cache)
+    assert torch.equal(out, out0) and torch.equal(lse, lse0)
