@@ -295,3 +295,23 @@ def test_page_harness_shapes_have_no_nan_rows(T, poison):
     cache[0] = 0
     out0, lse0 = run_attn(cfg, cache)
     assert torch.equal(out, out0) and torch.equal(lse, lse0)
+
+
+def test_single_entry_rows_and_an_all_padding_batch():
+    """Degenerate lists: width 1 (a row attends to one key, so its output is
+    that key's dequantised latent and its LSE that key's score; a -1 there
+    leaves the row empty), and a batch whose every entry is padding."""
+    cfg = dict(_tiny())
+    rng = np.random.default_rng(23)
+    T = 6
+    idx = rng.integers(1, cfg["num_slots"], size=(T, 1)).astype(np.int32)
+    idx[2, 0] = -1
+    cfg.update(T=T, H=4, W=1, idx=idx, q=wl.normal_bf16(rng, (T, 4, 576)))
+    cache = build_cache(cfg)
+    out, lse = run_attn(cfg, cache)
+    ref_out, ref_lse = oracle_for(cfg, range(T))
+    assert_parity(out, lse, ref_out, ref_lse, range(T))
+    assert torch.all(out[2] == 0) and bool(torch.isneginf(lse[2]).all())
+    pad = np.full((T, 300), -1, dtype=np.int32)
+    out, lse = run_attn(cfg, cache, idx=pad)
+    assert torch.all(out == 0) and bool(torch.isneginf(lse).all())
