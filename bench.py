@@ -482,6 +482,22 @@ def main():
         }
         sample = passes
         log(f"oracle: {dt:.2f} s for {sample} passes")
+        # the writer half of the metric: the oracle writer on the 8,192-row call
+        wc = wl.config_writer(N=8192, rope_dim=64)
+        wpasses, wdt = 0, 0.0
+        with threadpool_limits(limits=1):
+            while wdt < 3.0 and wpasses < 50:
+                wcache = wc["cache"].copy()
+                t0 = time.perf_counter()
+                owriter.kv_write(wcache, wc["latent"], wc["rope"], wc["slots"])
+                wdt += time.perf_counter() - t0
+                wpasses += 1
+        result["cpu_baseline_writer"] = {
+            "value": round(8192 * wpasses / (wdt * 1e6), 3), "unit": "rows/us", "cores": 1, "kind": "oracle",
+            "sample": f"float64 numpy oracle writer on the 8,192-row call (rope 64, a quarter padding rows), "
+                      f"{wpasses} passes in {wdt:.1f} s",
+        }
+        log(f"oracle writer: {wdt:.2f} s for {wpasses} passes")
     print(json.dumps(result), flush=True)
 
 
