@@ -86,6 +86,21 @@ def _check(call: str, rc: int) -> None:
         raise SparseMLAError(call, rc, lib().smla_last_error().decode())
 
 
+def _need(call: str, cond: bool, msg: str) -> None:
+    """Argument check of the binding; raises before anything is launched."""
+    if not cond:
+        raise ValueError(f"{call}: {msg}")
+
+
+def _same_device(call: str, ref_name: str, ref, **others) -> None:
+    """Every tensor must live on the reference tensor's GPU: a host tensor's
+    data_ptr() handed to a kernel would be dereferenced as a device address."""
+    _need(call, ref.is_cuda, f"{ref_name} must be a GPU tensor (it is on {ref.device})")
+    for name, t in others.items():
+        if t is not None:
+            _need(call, t.device == ref.device, f"{name} is on {t.device}, {ref_name} on {ref.device}")
+
+
 def _stream(t) -> int:
     import torch
     return torch.cuda.current_stream(t.device).cuda_stream
@@ -95,22 +110,59 @@ def _ptr(t) -> int | None:
     return None if t is None else t.data_ptr()
 
 
+def _check_rows_bf16(call: str, name: str, t, min_width: int) -> None:
+    import torch
+    _need(call, t.dtype == torch.bfloat16 and t.dim() == 2 and t.stride(1) == 1,
+          f"{name} must be a 2-D bf16 tensor with unit column stride")
+    _need(call, t.shape[1] >= min_width, f"{name} rows must hold >= {min_width} values (got {t.shape[1]})")
+
+
+def _check_out_lse(call: str, out, lse, T: int, H: int) -> None:
+    import torch
+    if out is not None:
+        _need(call, out.dtype == torch.bfloat16 and tuple(out.shape) == (T, H, LATENT) and out.is_contiguous(),
+              f"out must be a contiguous bf16 [{T}][{H}][{LATENT}] tensor")
+    if lse is not None:
+        _need(call, lse.dtype == torch.float32 and tuple(lse.shape) == (T, H) and lse.is_contiguous(),
+              f"lse must be a contiguous float32 [{T}][{H}] tensor")
+
+
+def _check_topk(call: str, topk_idx, T: int, topk_capacity) -> int:
+    import torch
+    _need(call, topk_idx.dtype == torch.int32 and topk_idx.dim() == 2 and topk_idx.stride(1) == 1,
+          "topk_idx must be a 2-D int32 tensor with unit column stride")
+    _need(call, topk_idx.shape[0] == T, f"topk_idx has {topk_idx.shape[0]} rows for {T} query rows")
+    W = topk_idx.shape[1] if topk_capacity is None else int(topk_capacity)
+    _need(call, 1 <= W <= topk_idx.shape[1],
+          f"topk_capacity {W} must be in [1, {topk_idx.shape[1]}] (the buffer's width)")
+    return W
+
+
+def _check_workspace(call: str, workspace) -> None:
+    if workspace is not None:
+        _need(call, workspace.is_contiguous(), "workspace must be contiguous")
+
+
 def kv_write(kv_c, k_pe, slot_mapping, kv_cache) -> None:
     """Quantise bf16 rows kv_c [N][>=512] (+ k_pe [N][>=64] or None) into
     kv_cache uint8 [num_slots][656] at slot_mapping int64 [N]; slot 0 dropped."""
     import torch
-    assert kv_c.dtype == torch.bfloat16 and kv_c.dim() == 2 and kv_c.stride(1) == 1
-    assert slot_mapping.dtype == torch.int64 and slot_mapping.is_contiguous()
-    assert kv_cache.dtype == torch.uint8 and kv_cache.is_contiguous() and kv_cache.shape[-1] == ROW_BYTES
-    rope_dim = 0
-    pe_stride = 0
-    if k_pe is not None:
-        assert k_pe.dtype == torch.bfloat16 and k_pe.dim() == 2 and k_pe.stride(1) == 1
-        rope_dim, pe_stride = 64, k_pe.stride(0)
+    call = "kv_write"
+    _check_rows_bf16(call, "kv_c", kv_c, LATENT)
     n = kv_c.shape[0]
-    num_slots = kv_cache.numel() // ROW_BYTES
+    _need(call, slot_mapping.dtype == torch.int64 and slot_mapping.dim() == 1 and slot_mapping.is_contiguous(),
+          "slot_mapping must be a contiguous 1-D int64 tensor")
+    _need(call, slot_mapping.shape[0] == n, f"slot_mapping has {slot_mapping.shape[0]} entries for {n} rows")
+    _need(call, kv_cache.dtype == torch.uint8 and kv_cache.dim() == 2 and kv_cache.is_contiguous()
+          and kv_cache.shape[1] == ROW_BYTES, f"kv_cache must be a contiguous uint8 [num_slots][{ROW_BYTES}] tensor")
+    rope_dim, pe_stride = 0, 0
+    if k_pe is not None:
+        _check_rows_bf16(call, "k_pe", k_pe, 64)
+        _need(call, k_pe.shape[0] == n, f"k_pe has {k_pe.shape[0]} rows for {n} rows of kv_c")
+        rope_dim, pe_stride = 64, k_pe.stride(0)
+    _same_device(call, "kv_cache", kv_cache, kv_c=kv_c, k_pe=k_pe, slot_mapping=slot_mapping)
     rc = lib().mla_kv_write(kv_c.data_ptr(), kv_c.stride(0), _ptr(k_pe), pe_stride, rope_dim,
-                            slot_mapping.data_ptr(), n, kv_cache.data_ptr(), num_slots,
+                            slot_mapping.data_ptr(), n, kv_cache.data_ptr(), kv_cache.shape[0],
                             _stream(kv_cache))
     _check("mla_kv_write", rc)
 
@@ -125,21 +177,28 @@ def attn(q, kv_cache, topk_idx, sm_scale: float, rope_dim: int, topk_capacity: i
     [num_slots][656]; topk_idx int32 [T][>=W] (row stride may exceed W).
     Returns (out bf16 [T][H][512], lse float32 [T][H] or None)."""
     import torch
-    assert q.dtype == torch.bfloat16 and q.dim() == 3 and q.is_contiguous()
+    call = "attn"
+    _need(call, rope_dim in (0, 64), f"rope_dim must be 0 or 64, got {rope_dim}")
+    _need(call, q.dtype == torch.bfloat16 and q.dim() == 3 and q.is_contiguous(),
+          "q must be a contiguous 3-D bf16 tensor")
     T, H, D = q.shape
-    assert D == LATENT + rope_dim
-    assert topk_idx.dtype == torch.int32 and topk_idx.dim() == 2 and topk_idx.stride(1) == 1
-    assert kv_cache.dtype == torch.uint8 and kv_cache.is_contiguous()
-    W = topk_idx.shape[1] if topk_capacity is None else int(topk_capacity)
+    _need(call, D == LATENT + rope_dim, f"q rows are {D} wide, expected {LATENT + rope_dim} for rope_dim {rope_dim}")
+    W = _check_topk(call, topk_idx, T, topk_capacity)
+    _need(call, kv_cache.dtype == torch.uint8 and kv_cache.dim() == 2 and kv_cache.is_contiguous()
+          and kv_cache.shape[1] == ROW_BYTES, f"kv_cache must be a contiguous uint8 [num_slots][{ROW_BYTES}] tensor")
+    _check_out_lse(call, out, lse, T, H)
+    _check_workspace(call, workspace)
+    _same_device(call, "q", q, kv_cache=kv_cache, topk_idx=topk_idx, out=out, lse=lse, workspace=workspace)
     if out is None:
         out = torch.empty((T, H, LATENT), dtype=torch.bfloat16, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
     need = workspace_size(T, H, W, rope_dim)
-    if need and (workspace is None or workspace.numel() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    rc = lib().sparse_mla_attn(q.data_ptr(), kv_cache.data_ptr(), kv_cache.numel() // ROW_BYTES,
+    if need and ws_bytes < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_bytes = need
+    rc = lib().sparse_mla_attn(q.data_ptr(), kv_cache.data_ptr(), kv_cache.shape[0],
                                topk_idx.data_ptr(), topk_idx.stride(0), W, T, H, rope_dim,
                                float(sm_scale), out.data_ptr(), _ptr(lse), _ptr(workspace),
                                ws_bytes, _stream(q))
@@ -151,10 +210,15 @@ def merge(part_out, part_lse, out=None, lse=None, want_lse: bool = True):
     """Merge P partial results: part_out bf16 [P][T][H][512], part_lse float32
     [P][T][H].  Returns (out bf16 [T][H][512], lse float32 [T][H] or None)."""
     import torch
-    assert part_out.dtype == torch.bfloat16 and part_out.dim() == 4 and part_out.is_contiguous()
+    call = "merge"
+    _need(call, part_out.dtype == torch.bfloat16 and part_out.dim() == 4 and part_out.is_contiguous(),
+          "part_out must be a contiguous 4-D bf16 tensor")
     P, T, H, D = part_out.shape
-    assert D == LATENT
-    assert part_lse.dtype == torch.float32 and part_lse.is_contiguous() and tuple(part_lse.shape) == (P, T, H)
+    _need(call, D == LATENT, f"part_out rows are {D} wide, expected {LATENT}")
+    _need(call, part_lse.dtype == torch.float32 and part_lse.is_contiguous() and tuple(part_lse.shape) == (P, T, H),
+          f"part_lse must be a contiguous float32 [{P}][{T}][{H}] tensor")
+    _check_out_lse(call, out, lse, T, H)
+    _same_device(call, "part_out", part_out, part_lse=part_lse, out=out, lse=lse)
     if out is None:
         out = torch.empty((T, H, LATENT), dtype=torch.bfloat16, device=part_out.device)
     if lse is None and want_lse:
@@ -170,13 +234,20 @@ def gather_upconvert(kv_cache, slots, rope_dim: int, out=None):
     into bf16 [N][576] (out may be a wider row-strided view); invalid slots give
     zero rows, NoPE rows zeros in columns 512..575."""
     import torch
-    assert kv_cache.dtype == torch.uint8 and kv_cache.is_contiguous() and kv_cache.shape[-1] == ROW_BYTES
-    assert slots.dtype == torch.int64 and slots.dim() == 1 and slots.is_contiguous()
+    call = "gather_upconvert"
+    _need(call, rope_dim in (0, 64), f"rope_dim must be 0 or 64, got {rope_dim}")
+    _need(call, kv_cache.dtype == torch.uint8 and kv_cache.dim() == 2 and kv_cache.is_contiguous()
+          and kv_cache.shape[1] == ROW_BYTES, f"kv_cache must be a contiguous uint8 [num_slots][{ROW_BYTES}] tensor")
+    _need(call, slots.dtype == torch.int64 and slots.dim() == 1 and slots.is_contiguous(),
+          "slots must be a contiguous 1-D int64 tensor")
     n = slots.shape[0]
+    if out is not None:
+        _check_rows_bf16(call, "out", out, LATENT + 64)
+        _need(call, out.shape[0] == n, f"out has {out.shape[0]} rows for {n} slots")
+    _same_device(call, "kv_cache", kv_cache, slots=slots, out=out)
     if out is None:
         out = torch.empty((n, LATENT + 64), dtype=torch.bfloat16, device=kv_cache.device)
-    assert out.dtype == torch.bfloat16 and out.dim() == 2 and out.stride(1) == 1 and out.shape[0] == n
-    rc = lib().mla_gather_upconvert(kv_cache.data_ptr(), kv_cache.numel() // ROW_BYTES, rope_dim,
+    rc = lib().mla_gather_upconvert(kv_cache.data_ptr(), kv_cache.shape[0], rope_dim,
                                     slots.data_ptr(), n, out.data_ptr(), out.stride(0),
                                     _stream(kv_cache))
     _check("mla_gather_upconvert", rc)
@@ -187,17 +258,24 @@ def kv_write_bf16(kv_c, k_pe, slot_mapping, kv_cache) -> None:
     """Store bf16 rows kv_c [N][>=512] (+ k_pe [N][>=64] or None) into the BF16
     cache kv_cache bf16 [num_slots][512 + rope_dim] at slot_mapping int64 [N]."""
     import torch
-    assert kv_c.dtype == torch.bfloat16 and kv_c.dim() == 2 and kv_c.stride(1) == 1
-    assert slot_mapping.dtype == torch.int64 and slot_mapping.is_contiguous()
+    call = "kv_write_bf16"
+    _check_rows_bf16(call, "kv_c", kv_c, LATENT)
+    n = kv_c.shape[0]
+    _need(call, slot_mapping.dtype == torch.int64 and slot_mapping.dim() == 1 and slot_mapping.is_contiguous(),
+          "slot_mapping must be a contiguous 1-D int64 tensor")
+    _need(call, slot_mapping.shape[0] == n, f"slot_mapping has {slot_mapping.shape[0]} entries for {n} rows")
     rope_dim, pe_stride = 0, 0
     if k_pe is not None:
-        assert k_pe.dtype == torch.bfloat16 and k_pe.dim() == 2 and k_pe.stride(1) == 1
+        _check_rows_bf16(call, "k_pe", k_pe, 64)
+        _need(call, k_pe.shape[0] == n, f"k_pe has {k_pe.shape[0]} rows for {n} rows of kv_c")
         rope_dim, pe_stride = 64, k_pe.stride(0)
-    assert kv_cache.dtype == torch.bfloat16 and kv_cache.is_contiguous()
-    assert kv_cache.shape[-1] == LATENT + rope_dim
+    _need(call, kv_cache.dtype == torch.bfloat16 and kv_cache.dim() == 2 and kv_cache.is_contiguous()
+          and kv_cache.shape[1] == LATENT + rope_dim,
+          f"kv_cache must be a contiguous bf16 [num_slots][{LATENT + rope_dim}] tensor")
+    _same_device(call, "kv_cache", kv_cache, kv_c=kv_c, k_pe=k_pe, slot_mapping=slot_mapping)
     rc = lib().mla_kv_write_bf16(kv_c.data_ptr(), kv_c.stride(0), _ptr(k_pe), pe_stride, rope_dim,
-                                 slot_mapping.data_ptr(), kv_c.shape[0], kv_cache.data_ptr(),
-                                 kv_cache.numel() // (LATENT + rope_dim), _stream(kv_cache))
+                                 slot_mapping.data_ptr(), n, kv_cache.data_ptr(),
+                                 kv_cache.shape[0], _stream(kv_cache))
     _check("mla_kv_write_bf16", rc)
 
 
@@ -207,22 +285,28 @@ def attn_bf16(q, kv_cache, topk_idx, sm_scale: float, topk_capacity: int | None 
     q bf16 [T][H][512 + rope_dim] (rope_dim 0 or 64, read from q's width);
     topk_idx int32 [T][>=W]."""
     import torch
-    assert q.dtype == torch.bfloat16 and q.dim() == 3 and q.is_contiguous()
-    rope_dim = q.shape[2] - LATENT
-    assert rope_dim in (0, 64)
-    assert kv_cache.dtype == torch.bfloat16 and kv_cache.is_contiguous() and kv_cache.shape[-1] == q.shape[2]
-    assert topk_idx.dtype == torch.int32 and topk_idx.dim() == 2 and topk_idx.stride(1) == 1
-    T, H, _ = q.shape
-    W = topk_idx.shape[1] if topk_capacity is None else int(topk_capacity)
+    call = "attn_bf16"
+    _need(call, q.dtype == torch.bfloat16 and q.dim() == 3 and q.is_contiguous(),
+          "q must be a contiguous 3-D bf16 tensor")
+    T, H, D = q.shape
+    rope_dim = D - LATENT
+    _need(call, rope_dim in (0, 64), f"q rows must be {LATENT} or {LATENT + 64} wide, got {D}")
+    _need(call, kv_cache.dtype == torch.bfloat16 and kv_cache.dim() == 2 and kv_cache.is_contiguous()
+          and kv_cache.shape[1] == D, f"kv_cache must be a contiguous bf16 [num_slots][{D}] tensor")
+    W = _check_topk(call, topk_idx, T, topk_capacity)
+    _check_out_lse(call, out, lse, T, H)
+    _check_workspace(call, workspace)
+    _same_device(call, "q", q, kv_cache=kv_cache, topk_idx=topk_idx, out=out, lse=lse, workspace=workspace)
     if out is None:
         out = torch.empty((T, H, LATENT), dtype=torch.bfloat16, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
     need = workspace_size(T, H, W, rope_dim)
-    if need and (workspace is None or workspace.numel() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    rc = lib().sparse_mla_attn_bf16(q.data_ptr(), kv_cache.data_ptr(), kv_cache.numel() // q.shape[2],
+    if need and ws_bytes < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_bytes = need
+    rc = lib().sparse_mla_attn_bf16(q.data_ptr(), kv_cache.data_ptr(), kv_cache.shape[0],
                                     topk_idx.data_ptr(), topk_idx.stride(0), W, T, H, rope_dim,
                                     float(sm_scale), out.data_ptr(), _ptr(lse), _ptr(workspace),
                                     ws_bytes, _stream(q))
@@ -235,10 +319,17 @@ def split_pages_64(src_pool, pages, dst, row_bytes: int = ROW_BYTES) -> None:
     into 64-token pages of dst (uint8 [>=4*num_src_pages][>=64*row_bytes], zeroed
     by the caller at allocation); pages int32 [n]."""
     import torch
-    assert src_pool.dtype == torch.uint8 and src_pool.dim() == 2 and src_pool.stride(1) == 1
-    assert dst.dtype == torch.uint8 and dst.dim() == 2 and dst.stride(1) == 1
-    assert pages.dtype == torch.int32 and pages.dim() == 1 and pages.is_contiguous()
-    assert dst.shape[0] >= 4 * src_pool.shape[0]
+    call = "split_pages_64"
+    _need(call, src_pool.dtype == torch.uint8 and src_pool.dim() == 2 and src_pool.stride(1) == 1,
+          "src_pool must be a 2-D uint8 tensor with unit column stride")
+    _need(call, dst.dtype == torch.uint8 and dst.dim() == 2 and dst.stride(1) == 1,
+          "dst must be a 2-D uint8 tensor with unit column stride")
+    _need(call, pages.dtype == torch.int32 and pages.dim() == 1 and pages.is_contiguous(),
+          "pages must be a contiguous 1-D int32 tensor")
+    _need(call, src_pool.shape[1] >= 256 * row_bytes, f"src_pool pages must hold 256 rows of {row_bytes} bytes")
+    _need(call, dst.shape[1] >= 64 * row_bytes, f"dst pages must hold 64 rows of {row_bytes} bytes")
+    _need(call, dst.shape[0] >= 4 * src_pool.shape[0], "dst must hold 4 pages per source page")
+    _same_device(call, "src_pool", src_pool, pages=pages, dst=dst)
     rc = lib().mla_split_pages_64(src_pool.data_ptr(), src_pool.shape[0], src_pool.stride(0),
                                   pages.data_ptr(), pages.shape[0], dst.data_ptr(), dst.stride(0),
                                   int(row_bytes), _stream(src_pool))

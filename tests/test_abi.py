@@ -191,3 +191,77 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=60)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+# ---- the Python binding refuses mismatched tensors before any launch ----------
+# Shape and dtype checks run before the device check, so host tensors exercise
+# them here; a host tensor with correct shapes is refused by the device check.
+
+def _bf(*shape):
+    import torch
+    return torch.zeros(shape, dtype=torch.bfloat16)
+
+
+def _raises(fn, *args, match, **kw):
+    with pytest.raises(ValueError, match=match):
+        fn(*args, **kw)
+
+
+def test_binding_kv_write_checks():
+    import torch
+    n = 8
+    kv_c, k_pe = _bf(n, 512), _bf(n, 64)
+    slots = torch.arange(1, n + 1, dtype=torch.int64)
+    cache = torch.zeros((64, 656), dtype=torch.uint8)
+    _raises(smla.kv_write, _bf(n, 500), None, slots, cache, match="kv_c rows must hold")
+    _raises(smla.kv_write, kv_c, None, slots[:5], cache, match="slot_mapping has 5 entries")
+    _raises(smla.kv_write, kv_c, None, slots.int(), cache, match="int64")
+    _raises(smla.kv_write, kv_c, _bf(n - 1, 64), slots, cache, match="k_pe has 7 rows")
+    _raises(smla.kv_write, kv_c, _bf(n, 32), slots, cache, match="k_pe rows must hold >= 64")
+    _raises(smla.kv_write, kv_c, k_pe, slots, torch.zeros((64, 528), dtype=torch.uint8), match="kv_cache")
+    _raises(smla.kv_write, kv_c, k_pe, slots, cache.view(8, 8, 656), match="kv_cache")
+    _raises(smla.kv_write, kv_c, k_pe, slots, cache, match="must be a GPU tensor")
+    _raises(smla.kv_write_bf16, kv_c, None, slots[:3], _bf(64, 512), match="slot_mapping has 3")
+    _raises(smla.kv_write_bf16, kv_c, k_pe, slots, _bf(64, 512), match=r"\[num_slots\]\[576\]")
+    _raises(smla.kv_write_bf16, kv_c, k_pe, slots, _bf(64, 576), match="must be a GPU tensor")
+
+
+def test_binding_attn_checks():
+    import torch
+    T, H = 4, 16
+    q = _bf(T, H, 512)
+    cache = torch.zeros((128, 656), dtype=torch.uint8)
+    idx = torch.full((T, 2176), -1, dtype=torch.int32)
+    _raises(smla.attn, q, cache, idx, 0.04, 64, match="q rows are 512 wide")
+    _raises(smla.attn, q, cache, idx, 0.04, 32, match="rope_dim must be 0 or 64")
+    _raises(smla.attn, q, cache, idx[:3], 0.04, 0, match="topk_idx has 3 rows for 4")
+    _raises(smla.attn, q, cache, idx, 0.04, 0, topk_capacity=2200, match="topk_capacity 2200")
+    _raises(smla.attn, q, cache, idx, 0.04, 0, topk_capacity=0, match="topk_capacity 0")
+    _raises(smla.attn, q, cache, idx.long(), 0.04, 0, match="int32")
+    _raises(smla.attn, q, cache[:, :528], idx, 0.04, 0, match="kv_cache")
+    _raises(smla.attn, q, cache, idx, 0.04, 0, out=_bf(T, H, 576), match="out must be")
+    _raises(smla.attn, q, cache, idx, 0.04, 0, lse=torch.zeros((T, H + 1)), match="lse must be")
+    _raises(smla.attn, q, cache, idx, 0.04, 0, match="q must be a GPU tensor")
+    _raises(smla.attn_bf16, q, _bf(128, 576), idx, 0.04, match=r"\[num_slots\]\[512\]")
+    _raises(smla.attn_bf16, _bf(T, H, 600), _bf(128, 600), idx, 0.04, match="512 or 576 wide")
+    _raises(smla.attn_bf16, q, _bf(128, 512), idx[:, :0], 0.04, match="topk_capacity 0")
+    _raises(smla.attn_bf16, q, _bf(128, 512), idx, 0.04, match="q must be a GPU tensor")
+
+
+def test_binding_other_checks():
+    import torch
+    cache = torch.zeros((128, 656), dtype=torch.uint8)
+    slots = torch.arange(4, dtype=torch.int64)
+    _raises(smla.gather_upconvert, cache, slots, 16, match="rope_dim")
+    _raises(smla.gather_upconvert, cache, slots, 0, out=_bf(3, 576), match="out has 3 rows for 4")
+    _raises(smla.gather_upconvert, cache, slots, 0, out=_bf(4, 512), match="out rows must hold >= 576")
+    _raises(smla.gather_upconvert, cache, slots, 0, match="must be a GPU tensor")
+    po, pl = _bf(2, 3, 16, 512), torch.zeros((2, 3, 16))
+    _raises(smla.merge, po, pl[:, :2], match="part_lse must be")
+    _raises(smla.merge, po, pl, out=_bf(3, 8, 512), match="out must be")
+    _raises(smla.merge, po, pl, match="must be a GPU tensor")
+    pool = torch.zeros((2, 256 * 656), dtype=torch.uint8)
+    pages = torch.zeros(2, dtype=torch.int32)
+    _raises(smla.split_pages_64, pool, pages, torch.zeros((7, 64 * 656), dtype=torch.uint8), match="4 pages per")
+    _raises(smla.split_pages_64, pool, pages, torch.zeros((8, 64 * 600), dtype=torch.uint8), match="64 rows")
+    _raises(smla.split_pages_64, pool, pages, torch.zeros((8, 64 * 656), dtype=torch.uint8), match="GPU tensor")
