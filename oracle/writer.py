@@ -109,3 +109,20 @@ def kv_write_bf16(cache_bits: np.ndarray, latent_bits: np.ndarray, rope_bits: np
             row = np.concatenate([row, np.asarray(rope_bits, dtype=np.uint16)[kept, :64]], axis=1)
         cache_bits[slots[kept]] = row
     return keep
+
+
+def unfiltered_kv_write(cache: np.ndarray, latent_bits: np.ndarray, rope_bits: np.ndarray | None,
+                        slots: np.ndarray) -> np.ndarray:
+    """NEGATIVE CONTROL ONLY: the zero-RoPE writer as it was before the fix of
+    sglang PR 47013 (Summary and Motivation), which drops no write aimed at the
+    reserved slot 0.  Every row with 0 <= slot < num_slots is packed and
+    stored, so the padding rows of a batch (undefined inputs, NaN here) land in
+    slot 0, the last of them winning.  Kept so that a test can show the slot-0
+    check failing for it while kv_write above passes."""
+    num_slots = cache.shape[0]
+    slots = np.asarray(slots, dtype=np.int64)
+    keep = (slots >= 0) & (slots < num_slots)
+    for i in np.nonzero(keep)[0]:                  # in row order: the last row for a slot wins
+        cache[slots[i]] = encode_rows(np.asarray(latent_bits)[i:i + 1],
+                                      None if rope_bits is None else np.asarray(rope_bits)[i:i + 1])[0]
+    return keep

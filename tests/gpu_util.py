@@ -13,8 +13,9 @@ from oracle import writer as oracle_writer
 DEV = "cuda:0"
 
 # Parity bar for attention outputs: max |o_gpu - o_ref| <= 2e-2 over all
-# elements, per-(row, head) relative L2 <= 1e-2, no NaN/Inf; lse within
-# 1e-3 * max(1, |lse|) (the LSE bar is this test suite's own addition).
+# elements, per-(row, head) relative L2 <= 1e-2, no NaN/Inf; lse within 1e-3
+# (this test suite's own addition; absolute, except relative to max(1, |lse|)
+# in the numerical stress tests, whose scores reach the hundreds).
 MAX_ABS = 2e-2
 MAX_REL_L2 = 1e-2
 MAX_LSE = 1e-3
@@ -87,10 +88,11 @@ def oracle_for(cfg: dict, rows, idx: np.ndarray | None = None, W: int | None = N
 
 
 def assert_parity(out: torch.Tensor, lse: torch.Tensor, ref_out, ref_lse, rows, abs_bound=None,
-                  unit_scale=True):
+                  unit_scale=True, lse_relative=False):
     """The parity bar on the listed query rows.  `abs_bound` (same shape as the
     selected outputs) adds an elementwise error bound; `unit_scale=False` drops
-    the absolute 2e-2 bar, which is only meaningful for unit-scale data."""
+    the absolute 2e-2 bar, which is only meaningful for unit-scale data;
+    `lse_relative=True` holds the LSE to 1e-3 * max(1, |lse|) instead of 1e-3."""
     rows = np.asarray(rows)
     o = to_f64(out)[rows]
     r = ref_out[rows]
@@ -112,6 +114,9 @@ def assert_parity(out: torch.Tensor, lse: torch.Tensor, ref_out, ref_lse, rows, 
         inf = np.isneginf(rl)
         assert np.array_equal(np.isneginf(g), inf)
         assert np.all(np.isfinite(g[~inf]))
-        # relative for large scores: fp32 score accumulation carries ~1e-5 relative error
-        d = np.abs(g[~inf] - rl[~inf]) / np.maximum(1.0, np.abs(rl[~inf]))
+        d = np.abs(g[~inf] - rl[~inf])
+        if lse_relative:
+            # stress data whose scores reach the hundreds: fp32 score
+            # accumulation carries ~1e-5 relative error, so the bar scales with |lse|
+            d = d / np.maximum(1.0, np.abs(rl[~inf]))
         assert d.size == 0 or d.max() <= MAX_LSE, f"lse err {d.max():.3e}"

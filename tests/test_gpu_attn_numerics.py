@@ -69,7 +69,8 @@ def _check(cfg, idx=None, unit_scale=True):
     ref = oracle_attn.sparse_mla_attn(cfg["q"], host_cache, idx, idx.shape[1],
                                       cfg["rope_dim"], cfg["sm_scale"])
     assert_parity(out, lse, ref[0], ref[1], range(cfg["T"]),
-                  abs_bound=_bound(cfg, host_cache, idx, ref[0]), unit_scale=unit_scale)
+                  abs_bound=_bound(cfg, host_cache, idx, ref[0]), unit_scale=unit_scale,
+                  lse_relative=True)
     return ref
 
 

@@ -128,3 +128,54 @@ def test_writer_workload_shape():
     assert not cache[written, 528:].any()
     untouched = np.setdiff1d(np.arange(1, 4096), written)
     assert np.all(cache[untouched] == 0xA5)
+
+
+def _slot_checks(cache, cfg):
+    """The checks of the writer workload: slot 0 left zero, the NoPE tail of
+    every written row zero, every other slot still 0xA5."""
+    written = cfg["slots"][cfg["slots"] > 0]
+    ok_slot0 = not cache[0].any()
+    ok_tail = cfg["rope_dim"] == 64 or not cache[written, 528:].any()
+    others = np.ones(cfg["num_slots"], dtype=bool)
+    others[0] = False
+    others[written] = False
+    ok_rest = bool((cache[others] == 0xA5).all())
+    return ok_slot0, ok_tail, ok_rest
+
+
+def test_negative_control_writer_without_the_slot0_skip():
+    """sglang PR 47013 (Modifications; Speed Tests, writer table with a quarter
+    of the rows aimed at slot 0): the check "slot 0 left zero" fails for the
+    writer before the fix and passes for the writer that drops slot-0 rows.
+    The pre-fix writer fills slot 0 with NaN codes (the padding rows carry NaN),
+    which the clamp-to-slot-0 reader then turns into NaN output in exactly the
+    rows that hold a -1 (sglang PR 39288, Root cause (1))."""
+    from oracle import attention
+    for rope_dim in (0, 64):
+        cfg = wl.config_writer(N=8192, rope_dim=rope_dim)
+        good = cfg["cache"].copy()
+        writer.kv_write(good, cfg["latent"], cfg["rope"], cfg["slots"])
+        assert _slot_checks(good, cfg) == (True, True, True)
+        bad = cfg["cache"].copy()
+        writer.unfiltered_kv_write(bad, cfg["latent"], cfg["rope"], cfg["slots"])
+        ok_slot0, ok_tail, ok_rest = _slot_checks(bad, cfg)
+        assert not ok_slot0 and ok_tail and ok_rest
+        # the NaN padding row became NaN codes and NaN scales in slot 0
+        assert set(np.unique(bad[0, :512] & 0x7F).tolist()) == {0x7F}
+        assert np.isnan(bad[0, 512:528].view("<f4")).all()
+        # rows 1.. of the real slots are identical under both writers
+        assert np.array_equal(bad[1:], good[1:])
+    # the faulty reader over the pre-fix cache: NaN rows are exactly the rows with a -1
+    rng = np.random.default_rng(3)
+    written = cfg["slots"][cfg["slots"] > 0]
+    T, H, W = 6, 4, 64
+    idx = np.full((T, W), -1, dtype=np.int32)
+    for t in range(T):
+        n = W if t % 2 == 0 else W - 5 * t
+        idx[t, :n] = rng.choice(written, size=n, replace=False)
+    q = wl.normal_bf16(rng, (T, H, 576))
+    o_bad = attention.clamped_gather_attn(q, bad, idx, W, 64, 1 / 24)
+    o_good, _ = attention.sparse_mla_attn(q, good, idx, W, 64, 1 / 24)
+    has_pad = (idx < 0).any(axis=1)
+    assert np.array_equal(np.isnan(o_bad).any(axis=(1, 2)), has_pad)
+    assert np.isfinite(o_good).all()
