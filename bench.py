@@ -44,7 +44,41 @@ def _args():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run plain device copies of 512 MiB (to scale HBM byte counters)")
+    ap.add_argument("--case", default=None,
+                    help="only time one attention workload (for profiling): " + ", ".join(CASES))
     return ap.parse_args()
+
+
+# single attention workloads that --case runs alone: (generator, first T rows or None)
+CASES = {
+    "nope_decode_T256": ("nope", 256), "nope_decode_T64": ("nope", 64),
+    "nope_decode_T16": ("nope", 16), "nope_decode_T1": ("nope", 1),
+    "rope_decode_T256": ("rope", 256), "rope_decode_T64": ("rope", 64),
+    "rope_decode_T16": ("rope", 16), "rope_decode_T1": ("rope", 1),
+    "nope_disjoint_T256": ("disjoint_nope", 256), "rope_disjoint_T256": ("disjoint_rope", 256),
+    "rope_disjoint_T64": ("disjoint64", 64),
+    "prefill_T65": ("prefill", 65), "prefill_T128": ("prefill", 128), "prefill_T1024": ("prefill", 1024),
+}
+
+
+def case_config(name):
+    import workloads as wl
+    kind, T = CASES[name]
+    if kind == "nope":
+        c = wl.config_nope_decode(64 if T < 256 else 256)
+    elif kind == "rope":
+        c = wl.config_rope_decode(256)
+    elif kind == "disjoint_nope":
+        return wl.config_disjoint_t256(0)
+    elif kind == "disjoint_rope":
+        return wl.config_disjoint_t256(64)
+    elif kind == "disjoint64":
+        return wl.config_disjoint(64)
+    else:
+        return wl.config_prefill(T)
+    c = dict(c)
+    c["q"], c["idx"] = c["q"][:T], c["idx"][:T]
+    return c
 
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -147,6 +181,18 @@ def main():
         idx = cfg["idx"]
         return int(((idx >= 0) & (idx < cfg["num_slots"])).sum()) * row_bytes
 
+    if a.case is not None:
+        log(f"case {a.case}")
+        c = case_config(a.case)
+        cache = build_cache(c)
+        rot = [cache] if a.case.startswith("prefill") else rotations(cache)
+        us, _, _ = time_attn(c, rot, a.steps, a.warmup)
+        b = gathered(c, ROPE_ROW if c["rope_dim"] else NOPE_ROW)
+        print(json.dumps({"case": a.case, "us": round(float(us.mean()), 2),
+                          "gathered_bytes": b, "gbs": round(b / (us.mean() * 1e-6) / 1e9, 1),
+                          "launches": a.steps + a.warmup}), flush=True)
+        return
+
     # ---------------- headline: NoPE decode T=256, writer + attention ---------------
     T = 256
     log("generating NoPE decode workload (T=256, 131072 slots)")
@@ -233,6 +279,10 @@ def main():
     attn_us = burst(lambda i: smla.attn(q, caches[i % len(caches)], idx, cfg["sm_scale"], 0,
                                         topk_capacity=W, out=out, lse=lse, workspace=ws),
                     a.steps, a.warmup)
+    # warm: the same cache copy every launch, so rows the previous launch
+    # gathered may still sit in the Infinity Cache
+    attn_warm = burst(lambda i: smla.attn(q, caches[0], idx, cfg["sm_scale"], 0, topk_capacity=W,
+                                          out=out, lse=lse, workspace=ws), a.steps, a.warmup)
     wr_us = burst(lambda i: smla.kv_write(new_lat, None, new_slots, caches[i % len(caches)]),
                   a.steps, a.warmup)
     value = bytes_step / (ms_per_step * 1e-3) / 1e9
@@ -266,6 +316,7 @@ def main():
         "attn_us": round(float(attn_us.mean()), 2),
         "attn_gbs": round(attn_gbs, 1),
         "attn_hbm_frac": round(attn_gbs / HBM_PEAK_GBS, 4),
+        "attn_warm_us": round(float(attn_warm.mean()), 2),
         "writer_step_us": round(float(wr_us.mean()), 3),
         "gathered_bytes_per_step": bytes_step,
         "unique_row_bytes_per_step": int(np.unique(cfg["idx"][cfg["idx"] >= 0]).size) * NOPE_ROW,
@@ -339,7 +390,24 @@ def main():
             log(f"nope T={Tc}: {us.mean():.1f} us")
         gather_extra("gather_upconvert_nope_N65536", rot, 0)
         del rot, cachec
-        # RoPE decode T=256 and the disjoint control
+        # the no-reuse controls: the headline batch shape with pairwise disjoint
+        # top-k sets on a 1,048,576-slot cache, so gathered bytes are unique
+        # bytes and every gathered row is read once per launch (NoPE in the
+        # 2176-wide buffer, RoPE in a 2048-wide one)
+        for name, rope_dim in (("nope_disjoint_T256", 0), ("rope_disjoint_T256", 64)):
+            log(f"generating {name}")
+            c = wl.config_disjoint_t256(rope_dim)
+            cache = build_cache(c)
+            rot = rotations(cache)
+            us, _, _ = time_attn(c, rot, a.steps, a.warmup)
+            b = gathered(c, ROPE_ROW if rope_dim else NOPE_ROW)
+            extras[name] = {"us": round(float(us.mean()), 2),
+                            "gbs": round(b / (us.mean() * 1e-6) / 1e9, 1),
+                            "hbm_frac": round(b / (us.mean() * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                            "gathered_bytes": b, "unique_row_bytes": b}
+            log(f"{name}: {us.mean():.1f} us")
+            del rot, cache, c
+        # RoPE decode T=256 and the smaller disjoint control
         for name, c in (("rope_decode_T256", wl.config_rope_decode(256)),
                         ("rope_disjoint_T64", wl.config_disjoint(64))):
             log(f"generating {name}")
@@ -463,41 +531,64 @@ def main():
         from threadpoolctl import threadpool_limits
         from oracle import attention as oattn
         from oracle import writer as owriter
+        # the host cores this process may run on, capped by the thread budget
+        # the environment grants (OMP_NUM_THREADS), which BLAS would use anyway
+        cores = len(os.sched_getaffinity(0))
+        if os.environ.get("OMP_NUM_THREADS", "").isdigit():
+            cores = min(cores, int(os.environ["OMP_NUM_THREADS"]))
         need = cfg["idx"].ravel()
         need = np.unique(need[need >= 0])
         ocache = np.zeros((cfg["num_slots"], wl.ROW_BYTES), dtype=np.uint8)
         ocache[need] = owriter.encode_rows(cfg["latent"][need - 1], None)
-        passes, dt = 0, 0.0
-        with threadpool_limits(limits=1):
-            while dt < 10.0 and passes < 50:     # about 10 s of host work
-                t0 = time.perf_counter()
-                oattn.sparse_mla_attn(cfg["q"], ocache, cfg["idx"], W, 0, cfg["sm_scale"])
-                dt += time.perf_counter() - t0
-                passes += 1
-        b = bytes_step * passes
+
+        def time_oracle_attn(threads, budget):
+            passes, dt = 0, 0.0
+            with threadpool_limits(limits=threads):
+                while dt < budget and passes < 50:
+                    t0 = time.perf_counter()
+                    oattn.sparse_mla_attn(cfg["q"], ocache, cfg["idx"], W, 0, cfg["sm_scale"])
+                    dt += time.perf_counter() - t0
+                    passes += 1
+            return passes, dt
+
+        def time_oracle_writer(wc, threads, budget):
+            passes, dt = 0, 0.0
+            with threadpool_limits(limits=threads):
+                while dt < budget and passes < 50:
+                    wcache = wc["cache"].copy()
+                    t0 = time.perf_counter()
+                    owriter.kv_write(wcache, wc["latent"], wc["rope"], wc["slots"])
+                    dt += time.perf_counter() - t0
+                    passes += 1
+            return passes, dt
+
+        passes, dt = time_oracle_attn(cores, 10.0)           # about 10 s of host work
         result["cpu_baseline"] = {
-            "value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "value": round(bytes_step * passes / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle",
             "sample": f"float64 numpy oracle attention over the whole 256-row NoPE decode batch, "
-                      f"{passes} passes in {dt:.1f} s, BLAS pinned to 1 thread",
+                      f"{passes} passes in {dt:.1f} s, BLAS threads = {cores} (the host cores "
+                      f"this process may use)",
         }
-        sample = passes
-        log(f"oracle: {dt:.2f} s for {sample} passes")
+        log(f"oracle ({cores} threads): {dt:.2f} s for {passes} passes")
+        p1, dt1 = time_oracle_attn(1, 5.0)
+        result["cpu_baseline_1thread"] = {
+            "value": round(bytes_step * p1 / dt1 / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"the same oracle attention, BLAS pinned to 1 thread, {p1} passes in {dt1:.1f} s",
+        }
+        log(f"oracle (1 thread): {dt1:.2f} s for {p1} passes")
         # the writer half of the metric: the oracle writer on the 8,192-row call
         wc = wl.config_writer(N=8192, rope_dim=64)
-        wpasses, wdt = 0, 0.0
-        with threadpool_limits(limits=1):
-            while wdt < 3.0 and wpasses < 50:
-                wcache = wc["cache"].copy()
-                t0 = time.perf_counter()
-                owriter.kv_write(wcache, wc["latent"], wc["rope"], wc["slots"])
-                wdt += time.perf_counter() - t0
-                wpasses += 1
-        result["cpu_baseline_writer"] = {
-            "value": round(8192 * wpasses / (wdt * 1e6), 3), "unit": "rows/us", "cores": 1, "kind": "oracle",
-            "sample": f"float64 numpy oracle writer on the 8,192-row call (rope 64, a quarter padding rows), "
-                      f"{wpasses} passes in {wdt:.1f} s",
-        }
-        log(f"oracle writer: {wdt:.2f} s for {wpasses} passes")
+        for key, threads, budget in (("cpu_baseline_writer", cores, 3.0),
+                                     ("cpu_baseline_writer_1thread", 1, 2.0)):
+            wp, wdt = time_oracle_writer(wc, threads, budget)
+            result[key] = {
+                "value": round(8192 * wp / (wdt * 1e6), 3), "unit": "rows/us", "cores": threads,
+                "kind": "oracle",
+                "sample": f"float64 numpy oracle writer on the 8,192-row call (rope 64, a quarter "
+                          f"padding rows), {wp} passes in {wdt:.1f} s, BLAS threads = {threads}",
+            }
+            log(f"oracle writer ({threads} threads): {wdt:.2f} s for {wp} passes")
     print(json.dumps(result), flush=True)
 
 

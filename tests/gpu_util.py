@@ -29,6 +29,14 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
     return t.float().cpu().numpy().astype(np.float64)
 
 
+def rows_of(cfg: dict, sel: np.ndarray) -> np.ndarray:
+    """Workload rows written to the slots `sel`: row i of the workload goes to
+    cfg["slots"][i], which the generators list in ascending order."""
+    rows = np.searchsorted(cfg["slots"], sel)
+    assert np.array_equal(cfg["slots"][rows], sel), "a needed slot has no workload row"
+    return rows
+
+
 def build_cache(cfg: dict, check_slots=None) -> torch.Tensor:
     """Writes every row of the workload through the HIP writer into a zeroed
     device cache, checks the written bytes against the oracle writer (all rows,
@@ -45,7 +53,7 @@ def build_cache(cfg: dict, check_slots=None) -> torch.Tensor:
     else:
         sel = np.unique(np.asarray(check_slots, dtype=np.int64))
         sel = sel[(sel >= 1) & (sel < num_slots)]
-    rows = sel - 1                          # workload row i is written to slot i + 1
+    rows = rows_of(cfg, sel)
     want = oracle_writer.encode_rows(cfg["latent"][rows],
                                      None if cfg["rope"] is None else cfg["rope"][rows])
     got = cache[torch.from_numpy(sel).to(DEV)].cpu().numpy()
@@ -60,8 +68,9 @@ def oracle_cache(cfg: dict, slots_needed) -> np.ndarray:
     cache = np.zeros((cfg["num_slots"], wl.ROW_BYTES), dtype=np.uint8)
     sel = np.unique(np.asarray(slots_needed, dtype=np.int64))
     sel = sel[(sel >= 1) & (sel < cfg["num_slots"])]
-    cache[sel] = oracle_writer.encode_rows(cfg["latent"][sel - 1],
-                                           None if cfg["rope"] is None else cfg["rope"][sel - 1])
+    rows = rows_of(cfg, sel)
+    cache[sel] = oracle_writer.encode_rows(cfg["latent"][rows],
+                                           None if cfg["rope"] is None else cfg["rope"][rows])
     cache[0] = cfg["slot0"]
     return cache
 

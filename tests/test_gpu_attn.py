@@ -102,6 +102,25 @@ def test_full_size_decode_every_row(kind):
     assert_parity(out, lse, ref_out, ref_lse, range(cfg["T"]))
 
 
+@pytest.mark.parametrize("rope_dim", [0, 64])
+def test_disjoint_t256_every_row(rope_dim):
+    """The no-reuse controls the benchmark times: 256 decode tokens whose
+    top-k sets are pairwise disjoint on a 1,048,576-slot cache (NoPE in the
+    2176-wide buffer, RoPE in a 2048-wide one), every row and head checked
+    against the oracle on the cache bytes the HIP writer produced."""
+    from oracle import attention as oracle_attn
+    print(f"disjoint T=256 rope={rope_dim}", flush=True)
+    cfg = wl.config_disjoint_t256(rope_dim)
+    rng = np.random.default_rng(6)
+    cache = build_cache(cfg, check_slots=rng.choice(cfg["slots"], size=4096, replace=False))
+    out, lse = run_attn(cfg, cache)
+    host = cache.cpu().numpy()
+    del cache
+    ref_out, ref_lse = oracle_attn.sparse_mla_attn(cfg["q"], host, cfg["idx"], cfg["idx"].shape[1],
+                                                   cfg["rope_dim"], cfg["sm_scale"])
+    assert_parity(out, lse, ref_out, ref_lse, range(cfg["T"]))
+
+
 @pytest.mark.parametrize("T", [63, 64, 65, 66, 128])
 def test_prefill_across_boundary(T):
     """Causal prefill rows (row t lists tokens <= t, then -1)."""

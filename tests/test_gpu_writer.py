@@ -117,10 +117,10 @@ def test_out_of_range_slots_are_dropped():
 def _tiles_below(amax_bits: int) -> np.ndarray:
     """Tiles of 128 bf16 values: element 0 is the tile maximum (amax_bits, so
     every tile has the same scale) and the rest run through every bf16 value
-    of smaller magnitude, both signs."""
+    of smaller magnitude, both signs, and -amax."""
     bits = np.arange(1 << 15, dtype=np.uint32)
     vals = bits[bits < amax_bits]
-    vals = np.concatenate([vals, vals | 0x8000]).astype(np.uint16)
+    vals = np.concatenate([vals, vals | 0x8000, [amax_bits | 0x8000]]).astype(np.uint16)
     n_tiles = (vals.size + 126) // 127
     tiles = np.zeros((n_tiles, 128), dtype=np.uint16)
     flat = np.zeros(n_tiles * 127, dtype=np.uint16)
@@ -130,16 +130,24 @@ def _tiles_below(amax_bits: int) -> np.ndarray:
     return tiles
 
 
-def test_every_bf16_value_at_many_scales():
-    """For 24 tile maxima (so 24 scales whose reciprocal is inexact), every
-    bf16 value below the maximum in magnitude is quantised: each quotient
-    x / scale, its e4m3 rounding and every tie that the scale produces are
-    compared byte for byte with the oracle."""
-    rng = np.random.default_rng(11)
-    exps = rng.integers(-60, 60, size=24)
-    mants = rng.integers(0, 128, size=24)
-    mants[:4] = [0, 1, 0x3F, 0x7F]
-    tiles = np.concatenate([_tiles_below(int(((e + 127) << 7) | m)) for e, m in zip(exps, mants)])
+# Biased bf16 exponents of the tile maximum swept over all 128 mantissas.  A
+# scale is fl32(amax / 448) with amax a bf16 value, so its mantissa takes only
+# 128 values per exponent.  The kernel's reciprocal fast path serves scales
+# >= 2^-60, i.e. amax >= 1.75 * 2^-52: exponent 75 (2^-52) straddles that
+# threshold at mantissa 96, 76 lies above it and 74 below; 254 holds the
+# largest finite maxima, 1 and 0 the smallest normal and the subnormal ones.
+SWEEP_EXPONENTS = [127, 254, 76, 75, 74, 1, 0]
+
+
+@pytest.mark.parametrize("amax_exp", SWEEP_EXPONENTS)
+def test_every_reachable_scale_byte_exact(amax_exp):
+    """Every tile maximum of one bf16 exponent (all 128 mantissas), each with
+    every smaller bf16 magnitude of both signs: every quotient x / scale the
+    writer can meet at these scales, its e4m3 rounding and every tie, is
+    compared byte for byte with the oracle writer."""
+    print(f"amax exponent {amax_exp}", flush=True)
+    tiles = np.concatenate([_tiles_below((amax_exp << 7) | m) for m in range(128)
+                            if (amax_exp, m) != (0, 0)])
     pad = (-tiles.shape[0]) % 4
     if pad:
         tiles = np.concatenate([tiles, tiles[:pad]])

@@ -179,3 +179,17 @@ def test_negative_control_writer_without_the_slot0_skip():
     has_pad = (idx < 0).any(axis=1)
     assert np.array_equal(np.isnan(o_bad).any(axis=(1, 2)), has_pad)
     assert np.isfinite(o_good).all()
+
+
+def test_writer_scale_sweep_covers_the_fast_path_threshold():
+    """The exponents of the GPU writer sweep reach scales on both sides of
+    2^-60 (the kernel's fast-path bound), and at each swept exponent the 128
+    maxima give 128 distinct float32 scales."""
+    from tests.test_gpu_writer import SWEEP_EXPONENTS
+    for e in SWEEP_EXPONENTS:
+        amax = [((e << 7) | m) for m in range(128) if (e, m) != (0, 0)]
+        f = (np.array(amax, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
+        scales = (f / 448.0).astype(np.float32)
+        assert np.unique(scales).size == len(amax)
+        if e == 75:
+            assert (scales >= 2.0 ** -60).sum() == 32 and (scales < 2.0 ** -60).sum() == 96

@@ -35,8 +35,9 @@ def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
 
     Inputs are finite (the generators only draw normals)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    u = x.view(np.uint32)
+    # finite inputs: |u| stays below 0x7F800000 per sign, so the sum cannot wrap
+    rounded = (u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) >> np.uint32(16)
     return rounded.astype(np.uint16)
 
 
@@ -182,16 +183,47 @@ def config_prefill(T: int, seed: int | None = None, num_slots: int = 131072,
 
 
 def config_disjoint(T: int = 64, seed: int = 60, num_slots: int = 262144,
-                    H: int = 16, W: int = 2048) -> dict:
-    """RoPE decode whose top-k sets are pairwise disjoint across the batch, so
-    gathered bytes equal unique bytes (a control against cache reuse)."""
+                    H: int = 16, W: int = 2048, rope_dim: int = ROPE, listed_only: bool = False,
+                    n_valid: int | None = None) -> dict:
+    """Decode whose top-k sets are pairwise disjoint across the batch, so
+    gathered bytes equal unique bytes (a control against cache reuse).
+
+    Default: the RoPE decode shape at T=64 on a 262,144-slot cache whose every
+    row is written.  With listed_only=True only the slots the top-k lists name
+    get rows (`slots` then holds those slot ids in ascending order, row i of
+    `latent` / `rope` going to slots[i]), which keeps a cache of a million
+    slots cheap to build; n_valid < W leaves the last W - n_valid entries of
+    every row -1 (the 2176-wide NoPE buffer with its 128-wide tail)."""
     rng = np.random.default_rng(seed)
-    latent, rope, slots = cache_rows(rng, num_slots, ROPE)
-    q = normal_bf16(rng, (T, H, LATENT + ROPE))
-    idx = disjoint_topk(rng, T, W, num_slots)
-    return dict(num_slots=num_slots, rope_dim=ROPE, T=T, H=H, W=W,
+    nv = W if n_valid is None else n_valid
+    if listed_only:
+        body = disjoint_topk(rng, T, nv, num_slots)
+        slots = np.sort(body.ravel()).astype(np.int64)
+        latent = normal_bf16(rng, (slots.size, LATENT))
+        rope = normal_bf16(rng, (slots.size, rope_dim)) if rope_dim else None
+        q = normal_bf16(rng, (T, H, LATENT + rope_dim))
+    else:
+        latent, rope, slots = cache_rows(rng, num_slots, rope_dim)
+        q = normal_bf16(rng, (T, H, LATENT + rope_dim))
+        body = disjoint_topk(rng, T, nv, num_slots)
+    idx = np.full((T, W), -1, dtype=np.int32)
+    idx[:, :nv] = body
+    return dict(num_slots=num_slots, rope_dim=rope_dim, T=T, H=H, W=W,
                 latent=latent, rope=rope, slots=slots, q=q, idx=idx,
-                sm_scale=float(1.0 / np.sqrt(LATENT + ROPE)), slot0=slot0_bytes(rng, "random"))
+                sm_scale=float(1.0 / np.sqrt(LATENT + rope_dim)),
+                slot0=slot0_bytes(rng, "random" if rope_dim else "7f"))
+
+
+def config_disjoint_t256(rope_dim: int) -> dict:
+    """The headline decode batch (256 tokens, H=16, top-k 2048) with pairwise
+    disjoint top-k sets on a 1,048,576-slot cache: 524,288 distinct slots, so
+    every gathered row is read once per call.  NoPE rows use the 2176-wide
+    buffer (2048 entries, then a 128-wide -1 tail), RoPE rows a 2048-wide one."""
+    if rope_dim:
+        return config_disjoint(T=256, seed=61, num_slots=1 << 20, W=2048, rope_dim=ROPE,
+                               listed_only=True)
+    return config_disjoint(T=256, seed=62, num_slots=1 << 20, W=2176, rope_dim=0,
+                           listed_only=True, n_valid=2048)
 
 
 def config_writer(N: int = 8192, rope_dim: int = ROPE, seed: int = 50,
