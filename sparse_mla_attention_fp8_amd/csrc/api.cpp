@@ -1,4 +1,5 @@
-// C ABI of the library: argument validation, workspace sizing and launches.
+// C ABI of the library: argument validation, workspace sizing and launches
+// (host code only).
 // Declarations and the contract of every entry point are in include/sparse_mla.h.
 #include <stdarg.h>
 #include <stdio.h>
@@ -21,7 +22,11 @@ int fail(int code, const char* fmt, ...) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-constexpr int kMaxRows = 65535;  // query rows per call: every launch grid stays below 2^31 workgroups
+constexpr int kMaxRows = 65535;  // query rows per call
+constexpr int64_t kMaxBlocks = 0x7FFFFFFF;   // workgroups of one launch grid
+// rows of the row-per-wavefront kernels (four rows per workgroup): at most
+// 4 * kMaxBlocks, written so that no comparison can overflow
+constexpr int64_t kMaxGridRows = 4 * kMaxBlocks;
 
 }  // namespace
 
@@ -38,7 +43,7 @@ int mla_kv_write(const void* kv_c, int64_t kv_c_row_stride, const void* k_pe,
   if (num_rows < 0) return fail(SMLA_EINVAL, "mla_kv_write: num_rows < 0");
   if (num_slots < 1) return fail(SMLA_EINVAL, "mla_kv_write: num_slots must be >= 1");
   if (num_rows == 0) return SMLA_OK;
-  if ((num_rows + 3) / 4 > 0x7FFFFFFF) return fail(SMLA_EUNSUPPORTED, "mla_kv_write: too many rows");
+  if (num_rows > kMaxGridRows) return fail(SMLA_EUNSUPPORTED, "mla_kv_write: too many rows");
   if (kv_c == nullptr || slot_mapping == nullptr || kv_cache == nullptr)
     return fail(SMLA_EINVAL, "mla_kv_write: null pointer argument");
   if (rope_dim == 64 && k_pe == nullptr)
@@ -70,7 +75,7 @@ int mla_kv_write_bf16(const void* kv_c, int64_t kv_c_row_stride, const void* k_p
   if (num_rows < 0) return fail(SMLA_EINVAL, "mla_kv_write_bf16: num_rows < 0");
   if (num_slots < 1) return fail(SMLA_EINVAL, "mla_kv_write_bf16: num_slots must be >= 1");
   if (num_rows == 0) return SMLA_OK;
-  if ((num_rows + 3) / 4 > 0x7FFFFFFF) return fail(SMLA_EUNSUPPORTED, "mla_kv_write_bf16: too many rows");
+  if (num_rows > kMaxGridRows) return fail(SMLA_EUNSUPPORTED, "mla_kv_write_bf16: too many rows");
   if (kv_c == nullptr || slot_mapping == nullptr || kv_cache == nullptr)
     return fail(SMLA_EINVAL, "mla_kv_write_bf16: null pointer argument");
   if (rope_dim == 64 && k_pe == nullptr)
@@ -97,7 +102,8 @@ size_t sparse_mla_attn_workspace_size(int T, int H, int topk_capacity, int rope_
   if (T < 1 || T > kMaxRows || H < 1 || H > SMLA_MAX_HEADS || topk_capacity < 1 ||
       (rope_dim != 0 && rope_dim != 64))
     return 0;
-  return smla::plan_attn(T, H, topk_capacity, rope_dim).workspace;
+  const smla::AttnPlan plan = smla::plan_attn(T, H, topk_capacity, rope_dim);
+  return plan.blocks > kMaxBlocks ? 0 : plan.workspace;
 }
 
 int sparse_mla_attn(const void* q, const void* kv_cache, int64_t num_slots,
@@ -122,6 +128,9 @@ int sparse_mla_attn(const void* q, const void* kv_cache, int64_t num_slots,
       (reinterpret_cast<uintptr_t>(topk_idx) & 3u) || (reinterpret_cast<uintptr_t>(lse) & 3u))
     return fail(SMLA_EINVAL, "sparse_mla_attn: misaligned pointer");
   const smla::AttnPlan plan = smla::plan_attn(T, H, topk_capacity, rope_dim);
+  if (plan.blocks > kMaxBlocks)
+    return fail(SMLA_EUNSUPPORTED, "sparse_mla_attn: %lld workgroups exceed one launch",
+                (long long)plan.blocks);
   if (plan.workspace > 0) {
     if (workspace == nullptr || workspace_bytes < plan.workspace)
       return fail(SMLA_EWORKSPACE, "sparse_mla_attn: workspace of %zu bytes needed, got %zu",
@@ -159,6 +168,9 @@ int sparse_mla_attn_bf16(const void* q, const void* kv_cache, int64_t num_slots,
       (reinterpret_cast<uintptr_t>(topk_idx) & 3u) || (reinterpret_cast<uintptr_t>(lse) & 3u))
     return fail(SMLA_EINVAL, "sparse_mla_attn_bf16: misaligned pointer");
   const smla::AttnPlan plan = smla::plan_attn(T, H, topk_capacity, rope_dim);
+  if (plan.blocks > kMaxBlocks)
+    return fail(SMLA_EUNSUPPORTED, "sparse_mla_attn_bf16: %lld workgroups exceed one launch",
+                (long long)plan.blocks);
   if (plan.workspace > 0) {
     if (workspace == nullptr || workspace_bytes < plan.workspace)
       return fail(SMLA_EWORKSPACE, "sparse_mla_attn_bf16: workspace of %zu bytes needed, got %zu",
@@ -183,7 +195,7 @@ int mla_gather_upconvert(const void* kv_cache, int64_t num_slots, int rope_dim,
   if (num_rows < 0) return fail(SMLA_EINVAL, "mla_gather_upconvert: num_rows < 0");
   if (num_slots < 1) return fail(SMLA_EINVAL, "mla_gather_upconvert: num_slots must be >= 1");
   if (num_rows == 0) return SMLA_OK;
-  if ((num_rows + 3) / 4 > 0x7FFFFFFF)
+  if (num_rows > kMaxGridRows)
     return fail(SMLA_EUNSUPPORTED, "mla_gather_upconvert: too many rows");
   if (kv_cache == nullptr || slots == nullptr || dst == nullptr)
     return fail(SMLA_EINVAL, "mla_gather_upconvert: null pointer argument");
@@ -208,7 +220,7 @@ int mla_split_pages_64(const void* src_pool, int64_t num_src_pages, int64_t src_
   if (num_src_pages < 1 || num_pages < 0)
     return fail(SMLA_EINVAL, "mla_split_pages_64: need num_src_pages >= 1 and num_pages >= 0");
   if (num_pages == 0) return SMLA_OK;
-  if (4 * num_pages > 0x7FFFFFFF) return fail(SMLA_EUNSUPPORTED, "mla_split_pages_64: too many pages");
+  if (num_pages > kMaxBlocks / 4) return fail(SMLA_EUNSUPPORTED, "mla_split_pages_64: too many pages");
   if (src_pool == nullptr || pages == nullptr || dst == nullptr)
     return fail(SMLA_EINVAL, "mla_split_pages_64: null pointer argument");
   if (src_page_stride < 256 * (int64_t)row_bytes || (src_page_stride & 15))
@@ -232,7 +244,7 @@ int sparse_mla_merge(const void* part_out, const float* part_lse, int P, int T, 
     return fail(SMLA_EINVAL, "sparse_mla_merge: need P >= 1, T >= 1 and 1 <= H <= %d (P=%d, T=%d, H=%d)",
                 SMLA_MAX_HEADS, P, T, H);
   const int64_t rows = (int64_t)T * H;
-  if ((rows + 3) / 4 > 0x7FFFFFFF)
+  if (rows > kMaxGridRows)
     return fail(SMLA_EUNSUPPORTED, "sparse_mla_merge: too many (row, head) pairs");
   if (part_out == nullptr || part_lse == nullptr || out == nullptr)
     return fail(SMLA_EINVAL, "sparse_mla_merge: null pointer argument");

@@ -55,10 +55,6 @@ namespace {
 
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
-constexpr int kHeads = 16;          // heads per workgroup (MFMA N)
-constexpr int kKeys = 64;           // keys per chunk (4 blocks of 16)
-constexpr int kMaxRange = 2304;     // top-k entries one split may own
-constexpr int kTargetBlocks = 256;  // one workgroup per CU (LDS-bound occupancy)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -1213,35 +1209,6 @@ hipError_t launch_merge(const float* part_o, const float* part_ml, int splits, i
 
 }  // namespace
 
-AttnPlan plan_attn(int T, int H, int W, int rope_dim) {
-  (void)rope_dim;
-  AttnPlan p{};
-  p.head_groups = (H + kHeads - 1) / kHeads;
-  const int units = T * p.head_groups;
-  const int max_splits = (W + kKeys - 1) / kKeys;
-  // at most one round of workgroups (one per CU): a split count that spills
-  // a few workgroups into a second round doubles the launch
-  int s = units >= kTargetBlocks ? 1 : kTargetBlocks / units;
-  s = s > max_splits ? max_splits : s;
-  if (W <= kMaxRange) {
-    // the whole row fits one scan: every split deals the row's valid entries
-    // out evenly (range 0), so padding in the buffer costs no split any work
-    p.splits = s;
-    p.range = s > 1 ? 0 : W;
-    p.workspace = (s > 1) ? (size_t)T * s * H * (kLatent + 2) * sizeof(float) : 0;
-    return p;
-  }
-  const int min_s = (W + kMaxRange - 1) / kMaxRange;
-  if (s < min_s) s = min_s;
-  int range = (W + s - 1) / s;
-  range = (range + kKeys - 1) / kKeys * kKeys;
-  s = (W + range - 1) / range;
-  p.splits = s;
-  p.range = range;
-  p.workspace = (s > 1) ? (size_t)T * s * H * (kLatent + 2) * sizeof(float) : 0;
-  return p;
-}
-
 hipError_t launch_attn(const uint16_t* q, const uint8_t* cache, int64_t num_slots,
                        const int32_t* idx, int64_t idx_stride, int W, int T, int H,
                        int rope_dim, float sm_scale, uint16_t* out, float* lse,
@@ -1252,7 +1219,7 @@ hipError_t launch_attn(const uint16_t* q, const uint8_t* cache, int64_t num_slot
     part_o = static_cast<float*>(workspace);
     part_ml = part_o + (size_t)T * plan.splits * H * kLatent;
   }
-  const int64_t blocks = (int64_t)plan.splits * T * plan.head_groups;
+  const int64_t blocks = plan.blocks;
   const float sl2 = sm_scale * kLog2e;
   // row byte offsets fit 32 bits (and slot * 656 fits the 24-bit multiply)
   const bool small = num_slots <= (int64_t)(0xFFFFFFFFull / kRowBytes) && num_slots < (1 << 24);
@@ -1281,7 +1248,7 @@ hipError_t launch_attn_bf16(const uint16_t* q, const uint16_t* cache, int64_t nu
     part_o = static_cast<float*>(workspace);
     part_ml = part_o + (size_t)T * plan.splits * H * kLatent;
   }
-  const int64_t blocks = (int64_t)plan.splits * T * plan.head_groups;
+  const int64_t blocks = plan.blocks;
   const float sl2 = sm_scale * kLog2e;
   // row byte offsets fit 32 bits
   const bool small = num_slots <= (int64_t)(0xFFFFFFFFull / (2 * (kLatent + rope_dim)));

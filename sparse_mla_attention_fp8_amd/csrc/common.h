@@ -13,6 +13,12 @@ constexpr int kScaleOff = 512;      // 4 x float32 tile scales
 constexpr int kRopeOff = 528;       // 64 x bf16 RoPE, or zeros for NoPE rows
 constexpr int kNopeRowBytes = 528;  // bytes a NoPE reader needs
 
+// Attention work decomposition, shared by the launch plan (host) and the kernels.
+constexpr int kHeads = 16;          // heads per workgroup (MFMA N)
+constexpr int kKeys = 64;           // keys per chunk (4 blocks of 16)
+constexpr int kMaxRange = 2304;     // top-k entries one split may own (LDS index list)
+constexpr int kTargetBlocks = 256;  // one workgroup per CU (LDS-bound occupancy)
+
 // Internal launchers (return a hipError_t from the launch).
 hipError_t launch_kv_write(const uint16_t* kv_c, int64_t kv_c_stride, const uint16_t* k_pe,
                            int64_t k_pe_stride, int rope_dim, const int64_t* slot_mapping,
@@ -31,6 +37,7 @@ struct AttnPlan {
   int splits;        // split-top-k count per (row, head group)
   int range;         // top-k entries per split (multiple of the chunk size); 0: every split
                      // scans the whole row and keeps an equal share of its valid entries
+  int64_t blocks;    // workgroups of the main launch (splits * T * head_groups)
   size_t workspace;  // bytes of partial results (0 when splits == 1)
 };
 AttnPlan plan_attn(int T, int H, int topk_capacity, int rope_dim);

@@ -1,0 +1,38 @@
+// Launch plan of the attention call (host only): a pure function of the
+// sizes, shared by the workspace query and the launch so the two agree.
+#include "common.h"
+
+namespace smla {
+
+AttnPlan plan_attn(int T, int H, int W, int rope_dim) {
+  (void)rope_dim;
+  AttnPlan p{};
+  p.head_groups = (H + kHeads - 1) / kHeads;
+  const int64_t units = (int64_t)T * p.head_groups;
+  const int64_t w = W;
+  const int64_t max_splits = (w + kKeys - 1) / kKeys;
+  // at most one round of workgroups (one per CU): a split count that spills
+  // a few workgroups into a second round doubles the launch
+  int64_t s = units >= kTargetBlocks ? 1 : kTargetBlocks / units;
+  s = s > max_splits ? max_splits : s;
+  int64_t range;
+  if (w <= kMaxRange) {
+    // the whole row fits one scan: every split deals the row's valid entries
+    // out evenly (range 0), so padding in the buffer costs no split any work
+    range = s > 1 ? 0 : w;
+  } else {
+    // wider buffers: fixed ranges of whole chunks, each at most one scan
+    const int64_t min_s = (w + kMaxRange - 1) / kMaxRange;
+    if (s < min_s) s = min_s;
+    range = (w + s - 1) / s;
+    range = (range + kKeys - 1) / kKeys * kKeys;
+    s = (w + range - 1) / range;
+  }
+  p.splits = (int)s;
+  p.range = (int)range;
+  p.blocks = s * units;
+  p.workspace = (s > 1) ? (size_t)T * (size_t)s * (size_t)H * (kLatent + 2) * sizeof(float) : 0;
+  return p;
+}
+
+}  // namespace smla
