@@ -14,6 +14,11 @@
  *
  *   mla_kv_write_bf16, sparse_mla_attn_bf16;
  *
+ * the attention call without a caller workspace, for callers that cannot
+ * allocate:
+ *
+ *   sparse_mla_attn_noalloc;
+ *
  * and three more around them:
  *
  *   mla_gather_upconvert  dequantises listed cache rows into a bf16 workspace
@@ -26,7 +31,8 @@
  *
  * Common rules
  *   - Every pointer argument is a DEVICE pointer owned by the caller; the
- *     library allocates nothing and keeps no device state between calls.
+ *     library allocates nothing and keeps no device state between calls,
+ *     except the per-GPU scratch array of sparse_mla_attn_noalloc.
  *   - Calls are asynchronous on `stream` (0 = the null stream) and do not
  *     synchronise.  They are reentrant; concurrent calls on different streams
  *     must not write the same memory.
@@ -152,6 +158,34 @@ int sparse_mla_attn(const void* q,
                     void* out, float* lse,
                     void* workspace, size_t workspace_bytes,
                     hipStream_t stream);
+
+/*
+ * sparse_mla_attn_noalloc - sparse_mla_attn without a caller workspace.
+ *
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * computation, kernels and arguments as sparse_mla_attn, minus the workspace:
+ * the split partials go to a scratch array of SMLA_NOALLOC_SCRATCH_BYTES that
+ * the library holds on every GPU it runs on until the process ends.  The call
+ * allocates nothing (no hipMalloc, no hipFree).  Its first use on a device
+ * looks the array's address up once (hipGetSymbolAddress, briefly making the
+ * stream's device current if it is not).
+ *
+ * Limit: sizes whose split partials would exceed the scratch, i.e.
+ * sparse_mla_attn_workspace_size(T, H, topk_capacity, rope_dim) >
+ * SMLA_NOALLOC_SCRATCH_BYTES, return SMLA_EWORKSPACE before any launch (every
+ * size with topk_capacity <= 2304 fits: it needs at most 8.03 MiB).
+ * All calls on one GPU share its scratch: calls that overlap on one GPU (on
+ * different streams, or from different threads) race and must not be issued.
+ * Nothing in the scratch needs to start at zero.
+ */
+#define SMLA_NOALLOC_SCRATCH_BYTES (16u << 20)
+int sparse_mla_attn_noalloc(const void* q,
+                            const void* kv_cache, int64_t num_slots,
+                            const int32_t* topk_idx, int64_t idx_row_stride, int topk_capacity,
+                            int T, int H, int rope_dim, float sm_scale,
+                            void* out, float* lse,
+                            hipStream_t stream);
 
 /*
  * mla_kv_write_bf16 - store MLA KV rows into a BF16 KV cache.

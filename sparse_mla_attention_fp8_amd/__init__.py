@@ -8,6 +8,8 @@ and a missing or unloadable library raises.
     kv_write(kv_c, k_pe, slot_mapping, kv_cache)
     attn(q, kv_cache, topk_idx, sm_scale, rope_dim, topk_capacity=None,
          out=None, lse=None, workspace=None) -> (out, lse)
+    attn_noalloc(q, kv_cache, topk_idx, sm_scale, rope_dim, topk_capacity=None,
+                 out, lse=None) -> (out, lse)
     merge(part_out, part_lse, out=None, lse=None) -> (out, lse)
     gather_upconvert(kv_cache, slots, rope_dim, out=None) -> out
     split_pages_64(src_pool, pages, dst, row_bytes=656)
@@ -23,6 +25,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsparse_mla.so")
 
 SMLA_OK, SMLA_EINVAL, SMLA_EWORKSPACE, SMLA_ELAUNCH, SMLA_EUNSUPPORTED = 0, -1, -2, -3, -4
+NOALLOC_SCRATCH_BYTES = 16 << 20
 ROW_BYTES = 656
 LATENT = 512
 
@@ -37,6 +40,10 @@ _SIGS = {
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "sparse_mla_attn_noalloc": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "mla_kv_write_bf16": (ctypes.c_int, [
         ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
         ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]),
@@ -203,6 +210,32 @@ def attn(q, kv_cache, topk_idx, sm_scale: float, rope_dim: int, topk_capacity: i
                                float(sm_scale), out.data_ptr(), _ptr(lse), _ptr(workspace),
                                ws_bytes, _stream(q))
     _check("sparse_mla_attn", rc)
+    return out, lse
+
+
+def attn_noalloc(q, kv_cache, topk_idx, sm_scale: float, rope_dim: int, out, lse=None,
+                 topk_capacity: int | None = None):
+    """sparse_mla_attn_noalloc: attn() without a workspace; the library's
+    per-GPU scratch holds the split partials, and the caller passes out (and
+    lse) so that the call allocates nothing.  Calls that overlap on one GPU
+    race on that scratch."""
+    import torch
+    call = "attn_noalloc"
+    _need(call, rope_dim in (0, 64), f"rope_dim must be 0 or 64, got {rope_dim}")
+    _need(call, q.dtype == torch.bfloat16 and q.dim() == 3 and q.is_contiguous(),
+          "q must be a contiguous 3-D bf16 tensor")
+    T, H, D = q.shape
+    _need(call, D == LATENT + rope_dim, f"q rows are {D} wide, expected {LATENT + rope_dim} for rope_dim {rope_dim}")
+    W = _check_topk(call, topk_idx, T, topk_capacity)
+    _need(call, kv_cache.dtype == torch.uint8 and kv_cache.dim() == 2 and kv_cache.is_contiguous()
+          and kv_cache.shape[1] == ROW_BYTES, f"kv_cache must be a contiguous uint8 [num_slots][{ROW_BYTES}] tensor")
+    _need(call, out is not None, "out must be given (the call allocates nothing)")
+    _check_out_lse(call, out, lse, T, H)
+    _same_device(call, "q", q, kv_cache=kv_cache, topk_idx=topk_idx, out=out, lse=lse)
+    rc = lib().sparse_mla_attn_noalloc(q.data_ptr(), kv_cache.data_ptr(), kv_cache.shape[0],
+                                       topk_idx.data_ptr(), topk_idx.stride(0), W, T, H, rope_dim,
+                                       float(sm_scale), out.data_ptr(), _ptr(lse), _stream(q))
+    _check("sparse_mla_attn_noalloc", rc)
     return out, lse
 
 

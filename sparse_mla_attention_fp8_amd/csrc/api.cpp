@@ -146,6 +146,53 @@ int sparse_mla_attn(const void* q, const void* kv_cache, int64_t num_slots,
   return SMLA_OK;
 }
 
+int sparse_mla_attn_noalloc(const void* q, const void* kv_cache, int64_t num_slots,
+                            const int32_t* topk_idx, int64_t idx_row_stride, int topk_capacity, int T,
+                            int H, int rope_dim, float sm_scale, void* out, float* lse,
+                            hipStream_t stream) {
+  g_err[0] = '\0';
+  if (rope_dim != 0 && rope_dim != 64)
+    return fail(SMLA_EINVAL, "sparse_mla_attn_noalloc: rope_dim must be 0 or 64, got %d", rope_dim);
+  if (T < 1 || H < 1 || H > SMLA_MAX_HEADS)
+    return fail(SMLA_EINVAL, "sparse_mla_attn_noalloc: need T >= 1 and 1 <= H <= %d (T=%d, H=%d)",
+                SMLA_MAX_HEADS, T, H);
+  if (T > kMaxRows)
+    return fail(SMLA_EUNSUPPORTED, "sparse_mla_attn_noalloc: at most %d query rows per call", kMaxRows);
+  if (topk_capacity < 1 || idx_row_stride < topk_capacity)
+    return fail(SMLA_EINVAL, "sparse_mla_attn_noalloc: need 1 <= topk_capacity <= idx_row_stride");
+  if (num_slots < 1) return fail(SMLA_EINVAL, "sparse_mla_attn_noalloc: num_slots must be >= 1");
+  if (!isfinite(sm_scale)) return fail(SMLA_EINVAL, "sparse_mla_attn_noalloc: sm_scale is not finite");
+  if (q == nullptr || kv_cache == nullptr || topk_idx == nullptr || out == nullptr)
+    return fail(SMLA_EINVAL, "sparse_mla_attn_noalloc: null pointer argument");
+  if (!aligned16(q) || !aligned16(kv_cache) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(topk_idx) & 3u) || (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return fail(SMLA_EINVAL, "sparse_mla_attn_noalloc: misaligned pointer");
+  const smla::AttnPlan plan = smla::plan_attn(T, H, topk_capacity, rope_dim);
+  if (plan.blocks > kMaxBlocks)
+    return fail(SMLA_EUNSUPPORTED, "sparse_mla_attn_noalloc: %lld workgroups exceed one launch",
+                (long long)plan.blocks);
+  static_assert(smla::kNoallocScratchBytes == SMLA_NOALLOC_SCRATCH_BYTES, "scratch size");
+  if (plan.workspace > smla::kNoallocScratchBytes)
+    return fail(SMLA_EWORKSPACE,
+                "sparse_mla_attn_noalloc: these sizes need %zu bytes of split partials, more than the "
+                "%zu-byte scratch; call sparse_mla_attn with a workspace instead",
+                plan.workspace, smla::kNoallocScratchBytes);
+  void* scratch = nullptr;
+  if (plan.workspace > 0) {
+    const hipError_t se = smla::noalloc_scratch(stream, &scratch);
+    if (se != hipSuccess)
+      return fail(SMLA_ELAUNCH, "sparse_mla_attn_noalloc: no scratch on the stream's device: %s",
+                  hipGetErrorString(se));
+  }
+  hipError_t e = smla::launch_attn(static_cast<const uint16_t*>(q),
+                                   static_cast<const uint8_t*>(kv_cache), num_slots, topk_idx,
+                                   idx_row_stride, topk_capacity, T, H, rope_dim, sm_scale,
+                                   static_cast<uint16_t*>(out), lse, scratch, plan, stream);
+  if (e != hipSuccess)
+    return fail(SMLA_ELAUNCH, "sparse_mla_attn_noalloc: launch failed: %s", hipGetErrorString(e));
+  return SMLA_OK;
+}
+
 int sparse_mla_attn_bf16(const void* q, const void* kv_cache, int64_t num_slots,
                          const int32_t* topk_idx, int64_t idx_row_stride, int topk_capacity, int T,
                          int H, int rope_dim, float sm_scale, void* out, float* lse,

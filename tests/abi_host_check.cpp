@@ -39,6 +39,8 @@ hipError_t launch_split_pages(const uint8_t*, int64_t, int64_t, const int32_t*, 
 hipError_t launch_merge(const uint16_t*, const float*, int, int64_t, uint16_t*, float*, hipStream_t) {
   ++g_launches; return g_result;
 }
+alignas(256) static unsigned char g_scratch_stub[256];
+hipError_t noalloc_scratch(hipStream_t, void** out) { *out = g_scratch_stub; return hipSuccess; }
 }  // namespace smla
 
 static int g_fail = 0;
@@ -140,6 +142,22 @@ int main() {
            SMLA_ELAUNCH);
     g_result = hipSuccess;
   }
+  // the allocation-free call: same checks, the scratch limit instead of a workspace
+  expect("noalloc ok", sparse_mla_attn_noalloc(P, Q, 4096, idx, 2176, 2176, 16, 16, 0, 0.04f, P, nullptr, s),
+         SMLA_OK);
+  expect("noalloc one split", sparse_mla_attn_noalloc(P, Q, 4096, idx, 2176, 2176, 256, 16, 0, 0.04f, P, nullptr,
+                                                      s), SMLA_OK);
+  expect("noalloc largest narrow plan", sparse_mla_attn_noalloc(P, Q, 4096, idx, 2304, 2304, 1, 128, 64, 0.04f, P,
+                                                                nullptr, s), SMLA_OK);
+  expect("noalloc too big", sparse_mla_attn_noalloc(P, Q, 4096, idx, 65536, 65536, 256, 16, 0, 0.04f, P, nullptr,
+                                                    s), SMLA_EWORKSPACE);
+  expect("noalloc W max", sparse_mla_attn_noalloc(P, Q, 4096, idx, INT_MAX, INT_MAX, 65535, 128, 0, 0.04f, P,
+                                                  nullptr, s), SMLA_EUNSUPPORTED);
+  expect("noalloc null", sparse_mla_attn_noalloc(P, Q, 4096, nullptr, 2176, 2176, 16, 16, 0, 0.04f, P, nullptr,
+                                                 s), SMLA_EINVAL);
+  expect("noalloc rope", sparse_mla_attn_noalloc(P, Q, 4096, idx, 2176, 2176, 16, 16, 1, 0.04f, P, nullptr, s),
+         SMLA_EINVAL);
+
   // the workspace query never overflows and agrees with the launch's checks
   for (int T : {1, 2, 3, 16, 64, 65, 255, 256, 257, 65535, 65536, INT_MAX, -1})
     for (int W : {1, 63, 64, 2048, 2176, 2304, 2305, 100000, INT_MAX, 0, -5})
