@@ -71,7 +71,9 @@ struct Geo {
   static constexpr int RB = ROPE ? 656 : 528;       // bytes staged per row
   static constexpr int NSEG = RB / 16;              // 16-byte segments per row
   static constexpr int STAGE = kKeys * RB;          // bytes per stage
-  static constexpr int NST = ROPE ? 3 : 4;          // ring depth: NST - 1 chunks in flight
+  static constexpr int NST = 3;                     // ring depth: NST - 1 chunks in flight
+  // q of a workgroup's 16 heads, rows padded by 16 bytes (see the q staging)
+  static constexpr int QBYTES = kHeads * (D * 2 + 16);
 };
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] at [15:14])
@@ -273,7 +275,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
 
   __shared__ __align__(16) uint8_t stages[G::NST * G::STAGE];   // ring of 64-row stages
   __shared__ int slot_list[kMaxRange];
-  __shared__ __align__(16) float4 xs[2][4][2][64];   // [chunk & 1][block][dim half][lane]: partial scores, keys 4g+r
+  // the staged q until every wavefront has split it, then the partial scores
+  // xs[chunk & 1][block][dim half][lane] (keys 4g + r of the block)
+  constexpr int kXsBytes = 2 * 4 * 2 * 64 * 16;
+  __shared__ __align__(16) uint8_t xq[G::QBYTES > kXsBytes ? G::QBYTES : kXsBytes];
+  float4 (*xs)[4][2][64] = reinterpret_cast<float4 (*)[4][2][64]>(xq);
   __shared__ int wave_counts[kScanRounds * kWaves];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -296,8 +302,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
   const int t = (int)(gridDim.x / (unsigned)(splits * head_groups)) - 1 - b / head_groups;
 
   // ---- q of the group's heads -> LDS (one copy per workgroup, issued before
-  // the index scan), rows padded by 16 bytes so the fragment reads below fall
-  // on distinct banks
+  // the index scan, into a buffer of its own so that the first gathers need not
+  // wait for it), rows padded by 16 bytes so the fragment reads below fall on
+  // distinct banks
   const int head = hg * kHeads + n16;
   const bool hvalid = head < H;
   {
@@ -306,7 +313,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
     constexpr int kInstr = (kHeads * kPitch + 63) / 64;
     const int nh = min(kHeads, H - hg * kHeads);
     const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(q + ((int64_t)t * H + hg * kHeads) * D);
-    const uint32_t lds_q = lds_addr(stages);
+    const uint32_t lds_q = lds_addr(xq);
 #pragma unroll
     for (int j = 0; j < (kInstr + kWaves - 1) / kWaves; ++j) {
       const int i = wave + kWaves * j;
@@ -327,65 +334,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
                     split, range == 0 ? splits : 0));
   const int nch = (n + kKeys - 1) / kKeys;
 
-  // q fragments of head n16: tile 2qh+u, dims 128(2qh+u) + 32g + 8k + [0, 8) -> qraw[4u + k]
-  uint4 qraw[8];
-  uint4 qpe_raw = make_uint4(0, 0, 0, 0);    // RoPE k-step qh: dims 512 + 32qh + 8g + [0, 8)
-  {
-    const uint8_t* qlds = stages + (size_t)n16 * (D * 2 + 16);
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        qraw[4 * u + k] = *reinterpret_cast<const uint4*>(qlds + 2 * (128 * (2 * qh + u) + 32 * g + 8 * k));
-    if (ROPE) qpe_raw = *reinterpret_cast<const uint4*>(qlds + 2 * (kLatent + 32 * qh + 8 * g));
-  }
 
-  if (!hvalid) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) qraw[i] = make_uint4(0, 0, 0, 0);
-    qpe_raw = make_uint4(0, 0, 0, 0);
-  }
-  // ---- q half -> e4m3 high + residual after a per-(head, half) power of two
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t w4[4] = {qraw[i].x, qraw[i].y, qraw[i].z, qraw[i].w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      amax = fmaxf(amax, fabsf(__uint_as_float(w4[j] << 16)));
-      amax = fmaxf(amax, fabsf(__uint_as_float(w4[j] & 0xFFFF0000u)));
-    }
-  }
-  amax = max_xg(amax);
-  int qe = 0;   // amax * 2^qe < 256
-  if (amax > 0.0f) {
-    qe = 134 - (int)((__float_as_uint(amax) >> 23) & 0xFF);
-    qe = qe > 126 ? 126 : (qe < -126 ? -126 : qe);
-  }
-  const float qscale = exp2_pow(qe);
-  // latent score = qs * sum_tiles scale_tile * <code, q_hi + q_lo>, already in log2 units
-  const float qs = exp2_pow(-qe) * sm_scale_log2;
-  i8v qhi[2], qlo[2];   // B operands of v_mfma_f32_16x16x128_f8f6f4, one per tile
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint4 w = qraw[4 * u + k];
-      const uint32_t w4[4] = {w.x, w.y, w.z, w.w};
-      float x[8];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        x[2 * j] = __uint_as_float(w4[j] << 16) * qscale;
-        x[2 * j + 1] = __uint_as_float(w4[j] & 0xFFFF0000u) * qscale;
-      }
-      uint32_t h0, l0, h1, l1;
-      split_e4m3(x[0], x[1], x[2], x[3], h0, l0);
-      split_e4m3(x[4], x[5], x[6], x[7], h1, l1);
-      qhi[u][2 * k] = (int)h0; qhi[u][2 * k + 1] = (int)h1;
-      qlo[u][2 * k] = (int)l0; qlo[u][2 * k + 1] = (int)l1;
-    }
-  }
-  const bf16x8 qpe = __builtin_bit_cast(bf16x8, qpe_raw);
+  // q, split below once the first gathers are in flight: latent score = qs *
+  // sum_tiles scale_tile * <code, q_hi + q_lo> (log2 units); qhi / qlo are the
+  // B operands of v_mfma_scale_f32_16x16x128_f8f6f4, one per tile; qpe the
+  // RoPE k-step's bf16 B operand
+  i8v qhi[2], qlo[2];
+  float qs;
+  bf16x8 qpe;
 
   // ---- gather geometry: instruction i = wave + 8j covers flat segments 64i + lane
   constexpr int CNT0 = (G::NSEG + kWaves - 1) / kWaves;
@@ -512,21 +468,83 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
   };
 
   // ---- pipeline: chunk c lives in stage c % NST ----
+  // The first NST chunks are issued as soon as the index list is in LDS; q is
+  // split while they are in flight.  Every compiler-visible global load (the
+  // index scan's) has been consumed by then, so the compiler has no reason to
+  // emit a vmcnt wait of its own in the loop (it does not count the inline-asm
+  // gathers; a wait of its own there would drain the whole pipeline).
   const uint32_t lds0 = lds_addr(stages);
-  // Every compiler-visible load is complete before the pipeline starts, so
-  // the compiler has no reason to emit a vmcnt wait of its own in the loop
-  // (it does not count the inline-asm gathers; a wait of its own there would
-  // drain the whole pipeline); and every wavefront has read its q fragments
-  // before the gathers overwrite the staged q.
-  __builtin_amdgcn_s_waitcnt(0);
-  lds_barrier();
+  if (nch > 0) {
+    fetch_slots(0);
+    issue(lds0, 0);
+  }
+
+  // q fragments of head n16: tile 2qh+u, dims 128(2qh+u) + 32g + 8k + [0, 8) -> qraw[4u + k]
+  uint4 qraw[8];
+  uint4 qpe_raw = make_uint4(0, 0, 0, 0);    // RoPE k-step qh: dims 512 + 32qh + 8g + [0, 8)
+  {
+    const uint8_t* qlds = xq + (size_t)n16 * (D * 2 + 16);
 #pragma unroll
-  for (int c = 0; c < G::NST; ++c)
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        qraw[4 * u + k] = *reinterpret_cast<const uint4*>(qlds + 2 * (128 * (2 * qh + u) + 32 * g + 8 * k));
+    if (ROPE) qpe_raw = *reinterpret_cast<const uint4*>(qlds + 2 * (kLatent + 32 * qh + 8 * g));
+  }
+
+  if (!hvalid) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qraw[i] = make_uint4(0, 0, 0, 0);
+    qpe_raw = make_uint4(0, 0, 0, 0);
+  }
+  // ---- q half -> e4m3 high + residual after a per-(head, half) power of two
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t w4[4] = {qraw[i].x, qraw[i].y, qraw[i].z, qraw[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      amax = fmaxf(amax, fabsf(__uint_as_float(w4[j] << 16)));
+      amax = fmaxf(amax, fabsf(__uint_as_float(w4[j] & 0xFFFF0000u)));
+    }
+  }
+  amax = max_xg(amax);
+  int qe = 0;   // amax * 2^qe < 256
+  if (amax > 0.0f) {
+    qe = 134 - (int)((__float_as_uint(amax) >> 23) & 0xFF);
+    qe = qe > 126 ? 126 : (qe < -126 ? -126 : qe);
+  }
+  const float qscale = exp2_pow(qe);
+  // latent score = qs * sum_tiles scale_tile * <code, q_hi + q_lo>, already in log2 units
+  qs = exp2_pow(-qe) * sm_scale_log2;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint4 w = qraw[4 * u + k];
+      const uint32_t w4[4] = {w.x, w.y, w.z, w.w};
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[2 * j] = __uint_as_float(w4[j] << 16) * qscale;
+        x[2 * j + 1] = __uint_as_float(w4[j] & 0xFFFF0000u) * qscale;
+      }
+      uint32_t h0, l0, h1, l1;
+      split_e4m3(x[0], x[1], x[2], x[3], h0, l0);
+      split_e4m3(x[4], x[5], x[6], x[7], h1, l1);
+      qhi[u][2 * k] = (int)h0; qhi[u][2 * k + 1] = (int)h1;
+      qlo[u][2 * k] = (int)l0; qlo[u][2 * k + 1] = (int)l1;
+    }
+  }
+  qpe = __builtin_bit_cast(bf16x8, qpe_raw);
+#pragma unroll
+  for (int c = 1; c < G::NST; ++c)
     if (c < nch) {
       fetch_slots(c);
       issue(lds0 + (uint32_t)(c * G::STAGE), c);
     }
   if (G::NST < nch) fetch_slots(G::NST);
+
   // chunk 0: wait for it (chunks 1 .. NST-1 stay in flight), score it, read its P.V operands
   if (nch > 0) {
     const int ahead = min(G::NST - 1, nch - 1);
