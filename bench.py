@@ -55,6 +55,7 @@ CASES = {
     "nope_decode_T16": ("nope", 16), "nope_decode_T1": ("nope", 1),
     "rope_decode_T256": ("rope", 256), "rope_decode_T64": ("rope", 64),
     "rope_decode_T16": ("rope", 16), "rope_decode_T1": ("rope", 1),
+    "nope_decode_T512": ("nope", 512), "rope_decode_T512": ("rope", 512),
     "nope_disjoint_T256": ("disjoint_nope", 256), "rope_disjoint_T256": ("disjoint_rope", 256),
     "rope_disjoint_T64": ("disjoint64", 64),
     "prefill_T65": ("prefill", 65), "prefill_T128": ("prefill", 128), "prefill_T1024": ("prefill", 1024),
@@ -65,9 +66,9 @@ def case_config(name):
     import workloads as wl
     kind, T = CASES[name]
     if kind == "nope":
-        c = wl.config_nope_decode(64 if T < 256 else 256)
+        c = wl.config_nope_decode(64 if T < 256 else T)
     elif kind == "rope":
-        c = wl.config_rope_decode(256)
+        c = wl.config_rope_decode(max(T, 256))
     elif kind == "disjoint_nope":
         return wl.config_disjoint_t256(0)
     elif kind == "disjoint_rope":

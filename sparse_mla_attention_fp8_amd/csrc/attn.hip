@@ -65,15 +65,27 @@ typedef __attribute__((address_space(3))) v2i lds_v2i;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
-template <int ROPE>
+// Geometry of the fp8 attention kernel for WAVES = 8 (64-key chunks, the two
+// key halves of a chunk on different wavefronts) or WAVES = 4 (32-key chunks,
+// every P.V wavefront over all keys of its tile; small enough for two
+// workgroups per CU).
+template <int ROPE, int WAVES>
 struct Geo {
   static constexpr int D = kLatent + ROPE;          // q width
   static constexpr int RB = ROPE ? 656 : 528;       // bytes staged per row
   static constexpr int NSEG = RB / 16;              // 16-byte segments per row
-  static constexpr int STAGE = kKeys * RB;          // bytes per stage
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int KEYS = 8 * WAVES;            // keys per chunk
+  static constexpr int NBLK = KEYS / 16;            // 16-key MFMA blocks per chunk
+  static constexpr int STAGE = KEYS * RB;           // bytes per stage
   static constexpr int NST = 3;                     // ring depth: NST - 1 chunks in flight
+  static constexpr int NI = (KEYS * NSEG + 63) / 64;   // 1-KB gather instructions per chunk
   // q of a workgroup's 16 heads, rows padded by 16 bytes (see the q staging)
   static constexpr int QBYTES = kHeads * (D * 2 + 16);
+  // four-wavefront workgroups stage q in the ring's last stage, which is
+  // filled only once q is split, to stay within half of the LDS
+  static constexpr bool Q_IN_STAGE = WAVES == 4;
+  static_assert(!Q_IN_STAGE || QBYTES <= STAGE, "q must fit a stage");
 };
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] at [15:14])
@@ -203,8 +215,8 @@ __device__ __forceinline__ long pack64(uint32_t lo, uint32_t hi) {
 }
 
 // Compacts the valid entries of idx[lo, hi) into list[] in buffer order and
-// returns their count.  In round r thread i takes entry lo + 512r + i, so each
-// wavefront's loads are contiguous and all five rounds are issued at once; a
+// returns their count.  In round r thread i takes entry lo + THREADS r + i, so
+// each wavefront's loads are contiguous and all rounds are issued at once; a
 // wavefront ballot per round gives its count, the counts of every (round,
 // wavefront) meet in LDS in buffer order, and each lane places its entry at its
 // group's base plus the valid lanes below it (mbcnt).  Two barriers in all.
@@ -212,13 +224,19 @@ __device__ __forceinline__ long pack64(uint32_t lo, uint32_t hi) {
 // With share_splits > 0 the valid entries are dealt out instead: of the n
 // valid entries of [lo, hi), split `split` keeps positions [split * share,
 // (split + 1) * share) in buffer order, share = ceil(n / share_splits)
-// rounded up to whole 64-key chunks, so the splits of a row get equal work
+// rounded up to whole KC-key chunks, so the splits of a row get equal work
 // wherever its padding sits.
-constexpr int kScanRounds = (kMaxRange + kThreads - 1) / kThreads;
+template <int THREADS>
+constexpr int scan_rounds() { return (kMaxRange + THREADS - 1) / THREADS; }
 
+template <int THREADS, int KC>
 __device__ int compact_valid(const int32_t* __restrict__ idx, int lo, int hi, int64_t num_slots,
-                             int* list, int* group_counts /* [kScanRounds * kWaves] */,
+                             int* list, int* group_counts /* [scan_rounds * waves] */,
                              int split = 0, int share_splits = 0) {
+  constexpr int kScanRounds = scan_rounds<THREADS>();
+  constexpr int kWaves = THREADS / 64;
+  constexpr int kThreads = THREADS;
+  constexpr int kKeys = KC;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int v[kScanRounds];
 #pragma unroll
@@ -264,23 +282,30 @@ __device__ int compact_valid(const int32_t* __restrict__ idx, int lo, int hi, in
 }
 
 // SMALL: the cache spans less than 4 GiB, so row byte offsets fit 32 bits.
-template <int ROPE, bool SMALL>
-__global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
+// WAVES: 8 (one workgroup per CU) or 4 (two per CU), see Geo.
+template <int ROPE, bool SMALL, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void attn_mfma_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ cache, int64_t num_slots,
     const int32_t* __restrict__ idx, int64_t idx_stride, int W, int H, float sm_scale_log2,
     int range, int splits, int head_groups, uint16_t* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ part_o, float* __restrict__ part_ml) {
-  using G = Geo<ROPE>;
+  using G = Geo<ROPE, WAVES>;
   constexpr int D = G::D, RB = G::RB;
+  constexpr int kWaves = WAVES;
+  constexpr int kKeys = G::KEYS;
+  constexpr int NB = G::NBLK;
 
-  __shared__ __align__(16) uint8_t stages[G::NST * G::STAGE];   // ring of 64-row stages
+  __shared__ __align__(16) uint8_t stages[G::NST * G::STAGE];   // ring of chunk stages
   __shared__ int slot_list[kMaxRange];
-  // the staged q until every wavefront has split it, then the partial scores
-  // xs[chunk & 1][block][dim half][lane] (keys 4g + r of the block)
-  constexpr int kXsBytes = 2 * 4 * 2 * 64 * 16;
-  __shared__ __align__(16) uint8_t xq[G::QBYTES > kXsBytes ? G::QBYTES : kXsBytes];
-  float4 (*xs)[4][2][64] = reinterpret_cast<float4 (*)[4][2][64]>(xq);
-  __shared__ int wave_counts[kScanRounds * kWaves];
+  // partial scores xs[chunk & 1][block][dim half][lane] (keys 4g + r of the
+  // block); with eight wavefronts this buffer first holds the staged q, until
+  // every wavefront has split it
+  constexpr int kXsBytes = 2 * NB * 2 * 64 * 16;
+  constexpr int kXqBytes = (!G::Q_IN_STAGE && G::QBYTES > kXsBytes) ? G::QBYTES : kXsBytes;
+  __shared__ __align__(16) uint8_t xq[kXqBytes];
+  float4 (*xs)[NB][2][64] = reinterpret_cast<float4 (*)[NB][2][64]>(xq);
+  __shared__ int wave_counts[scan_rounds<G::THREADS>() * kWaves];
+  uint8_t* const qstage = G::Q_IN_STAGE ? stages + (G::NST - 1) * G::STAGE : xq;
 
   const int tid = threadIdx.x, lane = tid & 63;
   // wave-uniform values are made visibly uniform so that every barrier sits on
@@ -288,10 +313,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n16 = lane & 15, g = lane >> 4;
   // QK role: 16 keys (block qb) x 256 dims (half qh, tiles 2qh and 2qh+1) plus
-  // RoPE k-step qh.  P.V role: tile pt, key half ps (keys 32ps..32ps+31 of
-  // each chunk); each key half keeps its own online-softmax state.
+  // RoPE k-step qh.  P.V role: tile pt over keys 32ps..32ps+31 of each chunk;
+  // with eight wavefronts each key half (ps) keeps its own online-softmax
+  // state, with four every wavefront takes the chunk's 32 keys (ps = 0).
   const int qb = wave >> 1, qh = wave & 1;
-  const int pt = wave >> 1, ps = wave & 1;
+  const int pt = WAVES == 8 ? wave >> 1 : wave;
+  const int ps = WAVES == 8 ? wave & 1 : 0;
   int b = blockIdx.x;
   const int split = b % splits;
   b /= splits;
@@ -313,7 +340,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
     constexpr int kInstr = (kHeads * kPitch + 63) / 64;
     const int nh = min(kHeads, H - hg * kHeads);
     const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(q + ((int64_t)t * H + hg * kHeads) * D);
-    const uint32_t lds_q = lds_addr(xq);
+    const uint32_t lds_q = lds_addr(qstage);
 #pragma unroll
     for (int j = 0; j < (kInstr + kWaves - 1) / kWaves; ++j) {
       const int i = wave + kWaves * j;
@@ -330,10 +357,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
   // (its barriers also publish the staged q: each wavefront's first wait for
   // its index loads covers its earlier q loads)
   const int n = __builtin_amdgcn_readfirstlane(
-      compact_valid(idx + (int64_t)t * idx_stride, lo_k, hi_k, num_slots, slot_list, wave_counts,
-                    split, range == 0 ? splits : 0));
+      compact_valid<G::THREADS, kKeys>(idx + (int64_t)t * idx_stride, lo_k, hi_k, num_slots, slot_list,
+                                       wave_counts, split, range == 0 ? splits : 0));
   const int nch = (n + kKeys - 1) / kKeys;
-
 
   // q, split below once the first gathers are in flight: latent score = qs *
   // sum_tiles scale_tile * <code, q_hi + q_lo> (log2 units); qhi / qlo are the
@@ -343,18 +369,23 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
   float qs;
   bf16x8 qpe;
 
-  // ---- gather geometry: instruction i = wave + 8j covers flat segments 64i + lane
-  constexpr int CNT0 = (G::NSEG + kWaves - 1) / kWaves;
-  constexpr int CNT1 = G::NSEG / kWaves;
-  const bool big = wave < G::NSEG % kWaves;      // issues CNT0 instructions, else CNT1
+  // ---- gather geometry: instruction i = wave + WAVES j covers flat segments
+  // 64i + lane of the chunk (a 32-key chunk ends halfway through its last
+  // instruction, whose upper 32 lanes load nothing)
+  constexpr int CNT0 = (G::NI + kWaves - 1) / kWaves;
+  constexpr int CNT1 = G::NI / kWaves;
+  const bool big = wave < G::NI % kWaves;        // issues CNT0 instructions, else CNT1
+  constexpr bool kWholeInstr = (kKeys * G::NSEG) % 64 == 0;   // no lane of an instruction idles
   const int my_cnt = big ? CNT0 : CNT1;
   // row and byte offset of each of this lane's segments (fixed for the kernel)
   int seg_row[CNT0], seg_off[CNT0];
+  bool seg_ok[CNT0];
 #pragma unroll
   for (int j = 0; j < CNT0; ++j) {
     const int f = 64 * (wave + kWaves * j) + lane;
-    seg_row[j] = f / G::NSEG;
-    seg_off[j] = (f - seg_row[j] * G::NSEG) * 16;
+    seg_ok[j] = f < kKeys * G::NSEG;
+    seg_row[j] = seg_ok[j] ? f / G::NSEG : 0;
+    seg_off[j] = seg_ok[j] ? (f - seg_row[j] * G::NSEG) * 16 : 0;
   }
   // Slots of the next chunk to gather, looked up one iteration ahead so that
   // the loads never wait on an LDS round trip (rows past the valid count take
@@ -375,7 +406,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
     (void)c;
 #pragma unroll
     for (int j = 0; j < CNT0; ++j) {
-      if (j < my_cnt) {
+      if (j < my_cnt && (kWholeInstr || seg_ok[j])) {
         const uint32_t lds = stage + 1024u * (uint32_t)(wave + kWaves * j);
         if (SMALL) {
           dma16_sbase(cache, __umul24((uint32_t)slot[j], (uint32_t)kRowBytes) + (uint32_t)seg_off[j], lds);
@@ -483,7 +514,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
   uint4 qraw[8];
   uint4 qpe_raw = make_uint4(0, 0, 0, 0);    // RoPE k-step qh: dims 512 + 32qh + 8g + [0, 8)
   {
-    const uint8_t* qlds = xq + (size_t)n16 * (D * 2 + 16);
+    const uint8_t* qlds = qstage + (size_t)n16 * (D * 2 + 16);
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -537,21 +568,28 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
     }
   }
   qpe = __builtin_bit_cast(bf16x8, qpe_raw);
+  // the other chunks of the ring, but not yet the stage that holds q
+  constexpr int kFirst = G::Q_IN_STAGE ? G::NST - 1 : G::NST;
 #pragma unroll
-  for (int c = 1; c < G::NST; ++c)
+  for (int c = 1; c < kFirst; ++c)
     if (c < nch) {
       fetch_slots(c);
       issue(lds0 + (uint32_t)(c * G::STAGE), c);
     }
-  if (G::NST < nch) fetch_slots(G::NST);
 
-  // chunk 0: wait for it (chunks 1 .. NST-1 stay in flight), score it, read its P.V operands
+  // chunk 0: wait for it (the chunks issued after it stay in flight), score
+  // it, read its P.V operands
   if (nch > 0) {
-    const int ahead = min(G::NST - 1, nch - 1);
+    const int ahead = min(kFirst - 1, nch - 1);
     if (ahead <= 0) vm_barrier<0>();
     else if (ahead == 1) { if (big) vm_barrier<CNT0>(); else vm_barrier<CNT1>(); }
-    else if (ahead == 2) { if (big) vm_barrier<2 * CNT0>(); else vm_barrier<2 * CNT1>(); }
-    else { if (big) vm_barrier<3 * CNT0>(); else vm_barrier<3 * CNT1>(); }
+    else { if (big) vm_barrier<2 * CNT0>(); else vm_barrier<2 * CNT1>(); }
+    // every wavefront has split q by now, so its stage can take its chunk
+    if (G::Q_IN_STAGE && G::NST - 1 < nch) {
+      fetch_slots(G::NST - 1);
+      issue(lds0 + (uint32_t)((G::NST - 1) * G::STAGE), G::NST - 1);
+    }
+    if (G::NST < nch) fetch_slots(G::NST);
     qk_finish(qk_mfma(qk_load(stages)), 0);
     read_pv(stages, va[0], sc[0]);
   }
@@ -680,31 +718,41 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
     step(c + 1, va[1], sc[1], va[0], sc[0]);
   }
 
-  // ---- combine the two key halves, then write ------------------------------
+  // ---- combine the two key halves (eight wavefronts), then write ------------
   const float post = exp2_pow(ne_run - 8);
   const float l_full = sum_xg(l_run) * post;
 #pragma unroll
   for (int cc = 0; cc < 8; ++cc)
 #pragma unroll
     for (int r = 0; r < 4; ++r) oacc[cc][r] *= post;
-  lds_barrier();                       // every wave is done with the stages
   float4* mo = reinterpret_cast<float4*>(stages);              // [c][pt][lane] partial O (32 KB)
   float2* ml = reinterpret_cast<float2*>(stages + 4 * 64 * 128);  // [pt][lane] (m, l)
   const int slot4 = pt * 64 + lane;
-  if (ps == 1) {
+  // with four wavefronts every P.V wavefront holds the whole row of its tile:
+  // its own state, weight 1, and nothing from another half
+  float M = m_run, L = l_full, w0 = 1.0f, w1 = 0.0f;
+  if constexpr (WAVES == 8) {
+    lds_barrier();                       // every wave is done with the stages
+    if (ps == 1) {
 #pragma unroll
-    for (int cc = 0; cc < 8; ++cc)
-      mo[cc * 256 + slot4] = make_float4(oacc[cc][0], oacc[cc][1], oacc[cc][2], oacc[cc][3]);
-    ml[slot4] = make_float2(m_run, l_full);
+      for (int cc = 0; cc < 8; ++cc)
+        mo[cc * 256 + slot4] = make_float4(oacc[cc][0], oacc[cc][1], oacc[cc][2], oacc[cc][3]);
+      ml[slot4] = make_float2(m_run, l_full);
+    }
+    lds_barrier();
+    if (ps == 1 || !hvalid) return;
+    const float2 o1 = ml[slot4];
+    M = fmaxf(m_run, o1.x);
+    // (a half without valid keys has l = 0, so its weight does not matter)
+    w0 = __builtin_amdgcn_exp2f(m_run - M);
+    w1 = __builtin_amdgcn_exp2f(o1.x - M);
+    L = w0 * l_full + w1 * o1.y;
+  } else {
+    if (!hvalid) return;
   }
-  lds_barrier();
-  if (ps == 1 || !hvalid) return;
-  const float2 o1 = ml[slot4];
-  const float M = fmaxf(m_run, o1.x);
-  // (a half without valid keys has l = 0, so its weight does not matter)
-  const float w0 = __builtin_amdgcn_exp2f(m_run - M);
-  const float w1 = __builtin_amdgcn_exp2f(o1.x - M);
-  const float L = w0 * l_full + w1 * o1.y;
+  auto other_half = [&](int cc) {
+    return WAVES == 8 ? mo[cc * 256 + slot4] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  };
   // oacc[c][r] (and mo) hold dim 128pt + 16c + 4g + r
   const int dim0 = 128 * pt + 4 * g;
   if (splits == 1) {
@@ -712,7 +760,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
     uint16_t* dst = out + ((int64_t)t * H + head) * kLatent + dim0;
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc) {
-      const float4 u = mo[cc * 256 + slot4];
+      const float4 u = other_half(cc);
       const float o4[4] = {w0 * oacc[cc][0] + w1 * u.x, w0 * oacc[cc][1] + w1 * u.y,
                            w0 * oacc[cc][2] + w1 * u.z, w0 * oacc[cc][3] + w1 * u.w};
       const uint32_t lo2 = (uint32_t)f32_to_bf16_rne(o4[0] * il) |
@@ -728,7 +776,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(
     float* dst = part_o + pidx * kLatent + dim0;
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc) {
-      const float4 u = mo[cc * 256 + slot4];
+      const float4 u = other_half(cc);
       *reinterpret_cast<float4*>(dst + 16 * cc) =
           make_float4(w0 * oacc[cc][0] + w1 * u.x, w0 * oacc[cc][1] + w1 * u.y,
                       w0 * oacc[cc][2] + w1 * u.z, w0 * oacc[cc][3] + w1 * u.w);
@@ -775,7 +823,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
   __shared__ __align__(16) uint8_t stages[kB16NST * kB16Stage];
   __shared__ int slot_list[kMaxRange];
   __shared__ __align__(16) float4 xs[2][4][2][64];
-  __shared__ int wave_counts[kScanRounds * kWaves];
+  __shared__ int wave_counts[scan_rounds<kThreads>() * kWaves];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -817,8 +865,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
   const int lo_k = range == 0 ? 0 : split * range;
   const int hi_k = range == 0 ? W : min(W, lo_k + range);
   const int n = __builtin_amdgcn_readfirstlane(
-      compact_valid(idx + (int64_t)t * idx_stride, lo_k, hi_k, num_slots, slot_list, wave_counts,
-                    split, range == 0 ? splits : 0));
+      compact_valid<kThreads, kKeys>(idx + (int64_t)t * idx_stride, lo_k, hi_k, num_slots, slot_list,
+                                     wave_counts, split, range == 0 ? splits : 0));
   const int nch = (n + kKeys - 1) / kKeys;
   // q fragments (B operand of the K-steps of half qh): dims 256qh + 32s + 8g + [0, 8)
   bf16x8 qf[8];
@@ -1242,14 +1290,22 @@ hipError_t launch_attn(const uint16_t* q, const uint8_t* cache, int64_t num_slot
   // row byte offsets fit 32 bits (and slot * 656 fits the 24-bit multiply)
   const bool small = num_slots <= (int64_t)(0xFFFFFFFFull / kRowBytes) && num_slots < (1 << 24);
   auto go = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, q, cache, num_slots,
-                       idx, idx_stride, W, H, sl2, plan.range, plan.splits, plan.head_groups, out,
-                       lse, part_o, part_ml);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(64 * plan.waves), 0, stream, q, cache,
+                       num_slots, idx, idx_stride, W, H, sl2, plan.range, plan.splits, plan.head_groups,
+                       out, lse, part_o, part_ml);
   };
-  if (rope_dim == 64) {
-    if (small) go(attn_mfma_kernel<64, true>); else go(attn_mfma_kernel<64, false>);
+  if (plan.waves == 4) {
+    if (rope_dim == 64) {
+      if (small) go(attn_mfma_kernel<64, true, 4>); else go(attn_mfma_kernel<64, false, 4>);
+    } else {
+      if (small) go(attn_mfma_kernel<0, true, 4>); else go(attn_mfma_kernel<0, false, 4>);
+    }
   } else {
-    if (small) go(attn_mfma_kernel<0, true>); else go(attn_mfma_kernel<0, false>);
+    if (rope_dim == 64) {
+      if (small) go(attn_mfma_kernel<64, true, 8>); else go(attn_mfma_kernel<64, false, 8>);
+    } else {
+      if (small) go(attn_mfma_kernel<0, true, 8>); else go(attn_mfma_kernel<0, false, 8>);
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.splits == 1) return e;

@@ -33,6 +33,9 @@ hipError_t launch_kv_write_bf16(const uint16_t* kv_c, int64_t kv_c_stride, const
 // Launch plan of the attention call; a pure function of the sizes, shared by
 // the workspace query and the launch so the two always agree.
 struct AttnPlan {
+  int waves;         // wavefronts per workgroup of the fp8 kernel: 8 (64-key chunks, one
+                     // workgroup per CU) or 4 (32-key chunks, two per CU) when the rows
+                     // outnumber one round of eight-wavefront workgroups
   int head_groups;   // ceil(H / 16)
   int splits;        // split-top-k count per (row, head group)
   int range;         // top-k entries per split (multiple of the chunk size); 0: every split

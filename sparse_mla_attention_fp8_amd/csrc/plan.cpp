@@ -30,6 +30,10 @@ AttnPlan plan_attn(int T, int H, int W, int rope_dim) {
   }
   p.splits = (int)s;
   p.range = (int)range;
+  // more (row, head group) units than one round of eight-wavefront workgroups:
+  // four-wavefront workgroups, two per CU, so that one's index load, q split
+  // and first gathers overlap the other's chunks
+  p.waves = units > kTargetBlocks ? 4 : 8;
   p.blocks = s * units;
   p.workspace = (s > 1) ? (size_t)T * (size_t)s * (size_t)H * (kLatent + 2) * sizeof(float) : 0;
   return p;

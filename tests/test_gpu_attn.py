@@ -334,3 +334,108 @@ def test_single_entry_rows_and_an_all_padding_batch():
     pad = np.full((T, 300), -1, dtype=np.int32)
     out, lse = run_attn(cfg, cache, idx=pad)
     assert torch.all(out == 0) and bool(torch.isneginf(lse).all())
+
+
+# ---- calls with more (row, head group) units than one round of eight-wavefront
+# workgroups run four-wavefront workgroups (32-key chunks, two per CU)
+
+@pytest.mark.parametrize("kind,T,H", [("nope", 300, 16), ("rope", 260, 32), ("rope", 257, 16)])
+def test_four_wave_decode_every_row(kind, T, H):
+    print(f"four-wave {kind} T={T} H={H}", flush=True)
+    if kind == "nope":
+        cfg = wl.config_nope_decode(T, seed=800 + T, num_slots=16384, ctx=(512, 16000), H=H)
+    else:
+        cfg = wl.config_rope_decode(T, seed=800 + T, num_slots=32768, ctx=(2048, 32000), H=H)
+    cache = build_cache(cfg)
+    out, lse = run_attn(cfg, cache)
+    rows = range(T)
+    ref_out, ref_lse = oracle_for(cfg, rows)
+    assert_parity(out, lse, ref_out, ref_lse, rows)
+
+
+def test_four_wave_chunk_edges_and_empty_rows():
+    """Rows of 0, 1, 31, 32, 33, 63, 64, 65 and more entries, padding spread
+    through the buffer, in a 300-row call (four-wavefront workgroups)."""
+    cfg = wl.config_rope_decode(300, seed=810, num_slots=16384, ctx=(600, 12000))
+    rng = np.random.default_rng(11)
+    idx = np.full((300, 2048), -1, dtype=np.int32)
+    counts = [0, 1, 31, 32, 33, 63, 64, 65, 95, 96, 97, 2048]
+    for t in range(300):
+        n = counts[t % len(counts)] if t < 120 else int(rng.integers(0, 2049))
+        pos = rng.choice(2048, size=n, replace=False)
+        idx[t, pos] = rng.choice(np.arange(1, 16384), size=n, replace=False)
+    cache = build_cache(cfg)
+    out, lse = run_attn(cfg, cache, idx=idx)
+    empty = np.nonzero((idx < 0).all(axis=1))[0]
+    assert empty.size > 0
+    assert torch.all(out[torch.from_numpy(empty).to(DEV)] == 0)
+    rows = range(300)
+    ref_out, ref_lse = oracle_for(cfg, rows, idx=idx)
+    assert_parity(out, lse, ref_out, ref_lse, rows)
+
+
+def test_four_wave_buffer_wider_than_one_scan():
+    """300 rows of a 3,000-wide buffer: fixed ranges of whole chunks (two splits
+    per row, merged), four-wavefront workgroups."""
+    cfg = wl.config_nope_decode(300, seed=820, num_slots=16384, ctx=(4000, 16000), W=3000)
+    rng = np.random.default_rng(12)
+    idx = np.full((300, 3000), -1, dtype=np.int32)
+    for t in range(300):
+        n = int(rng.integers(1, 2900))
+        pos = np.sort(rng.choice(3000, size=n, replace=False))
+        idx[t, pos] = rng.choice(np.arange(1, 16384), size=n, replace=False)
+    cache = build_cache(cfg)
+    out, lse = run_attn(cfg, cache, idx=idx)
+    rows = range(300)
+    ref_out, ref_lse = oracle_for(cfg, rows, idx=idx)
+    assert_parity(out, lse, ref_out, ref_lse, rows)
+
+
+def test_eight_and_four_wave_workgroups_agree():
+    """The first 256 rows of a 300-row call (four-wavefront workgroups) against
+    the same 256 rows alone (eight-wavefront workgroups, one per row)."""
+    cfg = wl.config_nope_decode(300, seed=830, num_slots=16384, ctx=(512, 16000))
+    cache = build_cache(cfg)
+    out300, lse300 = run_attn(cfg, cache)
+    c256 = dict(cfg)
+    c256["q"], c256["idx"] = cfg["q"][:256], cfg["idx"][:256]
+    out256, lse256 = run_attn(c256, cache)
+    assert (out300[:256].float() - out256.float()).abs().max().item() <= 2e-2
+    assert (lse300[:256] - lse256).abs().max().item() <= 1e-3
+
+
+@pytest.mark.parametrize("rope_dim", [0, 64])
+def test_four_wave_cache_beyond_4_gib(rope_dim):
+    """300 rows over a 7,000,000-slot cache (4.6 GB): the four-wavefront
+    kernel's 64-bit address path."""
+    from oracle import attention as oracle_attn
+    from oracle import writer as oracle_writer
+    print(f"four-wave cache beyond 4 GiB rope={rope_dim}", flush=True)
+    num_slots = 7_000_000
+    rng = np.random.default_rng(840 + rope_dim)
+    T, H, W = 300, 16, 96
+    idx = np.full((T, W), -1, dtype=np.int32)
+    for t in range(T):
+        n = 1 + t % W
+        v = rng.choice(num_slots - 6_600_000, size=n, replace=False) + 6_600_000      # beyond 4 GiB
+        v[: n // 2] = rng.choice(6_500_000 - 1, size=n // 2, replace=False) + 1
+        idx[t, :n] = v
+    slots = np.unique(idx[idx >= 0]).astype(np.int64)
+    latent = wl.normal_bf16(rng, (slots.size, 512))
+    rope = wl.normal_bf16(rng, (slots.size, rope_dim)) if rope_dim else None
+    cache = torch.empty((num_slots, wl.ROW_BYTES), dtype=torch.uint8, device=DEV)
+    cache[0] = 0x7F
+    lat_d = torch.from_numpy(latent.view(np.int16)).view(torch.bfloat16).to(DEV)
+    rope_d = torch.from_numpy(rope.view(np.int16)).view(torch.bfloat16).to(DEV) if rope_dim else None
+    smla.kv_write(lat_d, rope_d, torch.from_numpy(slots).to(DEV), cache)
+    q = wl.normal_bf16(rng, (T, H, 512 + rope_dim))
+    sm = float(1.0 / np.sqrt(512 + rope_dim))
+    out, lse = smla.attn(torch.from_numpy(q.view(np.int16)).view(torch.bfloat16).to(DEV), cache,
+                         torch.from_numpy(idx).to(DEV), sm, rope_dim)
+    torch.cuda.synchronize()
+    host = np.zeros((num_slots, wl.ROW_BYTES), dtype=np.uint8)
+    host[slots] = oracle_writer.encode_rows(latent, rope)
+    host[0] = 0x7F
+    ref_out, ref_lse = oracle_attn.sparse_mla_attn(q, host, idx, W, rope_dim, sm)
+    del cache
+    assert_parity(out, lse, ref_out, ref_lse, range(T))
