@@ -59,6 +59,9 @@ CASES = {
     "nope_disjoint_T256": ("disjoint_nope", 256), "rope_disjoint_T256": ("disjoint_rope", 256),
     "rope_disjoint_T64": ("disjoint64", 64),
     "prefill_T65": ("prefill", 65), "prefill_T128": ("prefill", 128), "prefill_T1024": ("prefill", 1024),
+    # the gather alone (smla_gather_rows_probe) over the same rows
+    "probe_nope_decode_T256": ("nope", 256), "probe_nope_disjoint_T256": ("disjoint_nope", 256),
+    "probe_rope_disjoint_T256": ("disjoint_rope", 256),
 }
 
 
@@ -182,12 +185,26 @@ def main():
         idx = cfg["idx"]
         return int(((idx >= 0) & (idx < cfg["num_slots"])).sum()) * row_bytes
 
+    def valid_list(cfg):
+        v = cfg["idx"].ravel()
+        return torch.from_numpy(np.ascontiguousarray(v[(v >= 0) & (v < cfg["num_slots"])])).to(dev)
+
+    def time_probe(cfg, caches, iters, warm):
+        """The gather alone over the call's valid entries (the attention's rows)."""
+        sl = valid_list(cfg)
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        return burst(lambda i: smla.gather_rows_probe(caches[i % len(caches)], sl, cfg["rope_dim"], sink),
+                     iters, warm)
+
     if a.case is not None:
         log(f"case {a.case}")
         c = case_config(a.case)
         cache = build_cache(c)
         rot = [cache] if a.case.startswith("prefill") else rotations(cache)
-        us, _, _ = time_attn(c, rot, a.steps, a.warmup)
+        if a.case.startswith("probe_"):
+            us = time_probe(c, rot, a.steps, a.warmup)
+        else:
+            us, _, _ = time_attn(c, rot, a.steps, a.warmup)
         b = gathered(c, ROPE_ROW if c["rope_dim"] else NOPE_ROW)
         print(json.dumps({"case": a.case, "us": round(float(us.mean()), 2),
                           "gathered_bytes": b, "gbs": round(b / (us.mean() * 1e-6) / 1e9, 1),
@@ -286,6 +303,7 @@ def main():
                                           out=out, lse=lse, workspace=ws), a.steps, a.warmup)
     wr_us = burst(lambda i: smla.kv_write(new_lat, None, new_slots, caches[i % len(caches)]),
                   a.steps, a.warmup)
+    probe_us = time_probe(cfg, caches, a.steps, a.warmup)
     value = bytes_step / (ms_per_step * 1e-3) / 1e9
     attn_gbs = bytes_step / (attn_us.mean() * 1e-6) / 1e9
     log(f"step {ms_per_step*1e3:.1f} us, attention {attn_us.mean():.1f} us "
@@ -318,6 +336,8 @@ def main():
         "attn_gbs": round(attn_gbs, 1),
         "attn_hbm_frac": round(attn_gbs / HBM_PEAK_GBS, 4),
         "attn_warm_us": round(float(attn_warm.mean()), 2),
+        "gather_only_us": round(float(probe_us.mean()), 2),
+        "attn_over_gather_only": round(float(probe_us.mean() / attn_us.mean()), 4),
         "writer_step_us": round(float(wr_us.mean()), 3),
         "gathered_bytes_per_step": bytes_step,
         "unique_row_bytes_per_step": int(np.unique(cfg["idx"][cfg["idx"] >= 0]).size) * NOPE_ROW,
@@ -401,11 +421,15 @@ def main():
             cache = build_cache(c)
             rot = rotations(cache)
             us, _, _ = time_attn(c, rot, a.steps, a.warmup)
+            pus = time_probe(c, rot, a.steps, a.warmup)
             b = gathered(c, ROPE_ROW if rope_dim else NOPE_ROW)
             extras[name] = {"us": round(float(us.mean()), 2),
                             "gbs": round(b / (us.mean() * 1e-6) / 1e9, 1),
                             "hbm_frac": round(b / (us.mean() * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                            "gathered_bytes": b, "unique_row_bytes": b}
+                            "gathered_bytes": b, "unique_row_bytes": b,
+                            "gather_only_us": round(float(pus.mean()), 2),
+                            "gather_only_hbm_frac": round(b / (pus.mean() * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                            "attn_over_gather_only": round(float(pus.mean() / us.mean()), 4)}
             log(f"{name}: {us.mean():.1f} us")
             del rot, cache, c
         # RoPE decode T=256 and the smaller disjoint control

@@ -60,6 +60,9 @@ _SIGS = {
     "sparse_mla_merge": (ctypes.c_int, [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "smla_gather_rows_probe": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+        ctypes.c_void_p, ctypes.c_void_p]),
     "smla_last_error": (ctypes.c_char_p, []),
 }
 
@@ -367,3 +370,24 @@ def split_pages_64(src_pool, pages, dst, row_bytes: int = ROW_BYTES) -> None:
                                   pages.data_ptr(), pages.shape[0], dst.data_ptr(), dst.stride(0),
                                   int(row_bytes), _stream(src_pool))
     _check("mla_split_pages_64", rc)
+
+
+def gather_rows_probe(kv_cache, slots, rope_dim: int, sink=None):
+    """smla_gather_rows_probe: read the bytes of the listed rows (int32 slots
+    [n]) that an attention call gathers, with no arithmetic; for measuring the
+    gather ceiling of a list of rows.  Returns the uint32 sink tensor."""
+    import torch
+    call = "gather_rows_probe"
+    _need(call, rope_dim in (0, 64), f"rope_dim must be 0 or 64, got {rope_dim}")
+    _need(call, kv_cache.dtype == torch.uint8 and kv_cache.dim() == 2 and kv_cache.is_contiguous()
+          and kv_cache.shape[1] == ROW_BYTES, f"kv_cache must be a contiguous uint8 [num_slots][{ROW_BYTES}] tensor")
+    _need(call, slots.dtype == torch.int32 and slots.dim() == 1 and slots.is_contiguous(),
+          "slots must be a contiguous 1-D int32 tensor")
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=kv_cache.device)
+    _need(call, sink.numel() >= 1 and sink.element_size() == 4, "sink must hold one 32-bit word")
+    _same_device(call, "kv_cache", kv_cache, slots=slots, sink=sink)
+    rc = lib().smla_gather_rows_probe(kv_cache.data_ptr(), kv_cache.shape[0], rope_dim, slots.data_ptr(),
+                                      slots.shape[0], sink.data_ptr(), _stream(kv_cache))
+    _check("smla_gather_rows_probe", rc)
+    return sink

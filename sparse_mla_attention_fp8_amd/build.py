@@ -15,7 +15,7 @@ LIB = os.path.join(PKG, "libsparse_mla.so")
 # device code (hipcc, gfx950) and host-only code (the C ABI's validation and
 # the launch plan, plain C++ built by the host compiler)
 SOURCES = ["kv_write.hip", "attn.hip", "merge.hip", "gather.hip", "split_pages.hip",
-           "noalloc.hip", "api.cpp", "plan.cpp"]
+           "noalloc.hip", "measure.hip", "api.cpp", "plan.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CXX = os.environ.get("CXX", "g++")

@@ -6,6 +6,7 @@
 #include <math.h>
 
 #include "../../include/sparse_mla.h"
+#include "../../include/sparse_mla_measure.h"
 #include "common.h"
 
 namespace {
@@ -302,6 +303,29 @@ int sparse_mla_merge(const void* part_out, const float* part_lse, int P, int T, 
                                     static_cast<uint16_t*>(out), lse, stream);
   if (e != hipSuccess)
     return fail(SMLA_ELAUNCH, "sparse_mla_merge: launch failed: %s", hipGetErrorString(e));
+  return SMLA_OK;
+}
+
+int smla_gather_rows_probe(const void* kv_cache, int64_t num_slots, int rope_dim, const int32_t* slots,
+                           int64_t n, uint32_t* sink, hipStream_t stream) {
+  g_err[0] = '\0';
+  if (rope_dim != 0 && rope_dim != 64)
+    return fail(SMLA_EINVAL, "smla_gather_rows_probe: rope_dim must be 0 or 64, got %d", rope_dim);
+  if (n < 0 || num_slots < 1)
+    return fail(SMLA_EINVAL, "smla_gather_rows_probe: need n >= 0 and num_slots >= 1");
+  if (n > smla::gather_probe_max_rows())
+    return fail(SMLA_EUNSUPPORTED, "smla_gather_rows_probe: at most %lld rows",
+                (long long)smla::gather_probe_max_rows());
+  if (n == 0) return SMLA_OK;
+  if (kv_cache == nullptr || slots == nullptr || sink == nullptr)
+    return fail(SMLA_EINVAL, "smla_gather_rows_probe: null pointer argument");
+  if (!aligned16(kv_cache) || (reinterpret_cast<uintptr_t>(slots) & 3u) ||
+      (reinterpret_cast<uintptr_t>(sink) & 3u))
+    return fail(SMLA_EINVAL, "smla_gather_rows_probe: misaligned pointer");
+  hipError_t e = smla::launch_gather_probe(static_cast<const uint8_t*>(kv_cache), num_slots, rope_dim, slots,
+                                           n, sink, stream);
+  if (e != hipSuccess)
+    return fail(SMLA_ELAUNCH, "smla_gather_rows_probe: launch failed: %s", hipGetErrorString(e));
   return SMLA_OK;
 }
 

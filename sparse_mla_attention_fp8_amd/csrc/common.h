@@ -66,6 +66,11 @@ hipError_t launch_split_pages(const uint8_t* src, int64_t num_src_pages, int64_t
 hipError_t launch_merge(const uint16_t* part_out, const float* part_lse, int P, int64_t rows,
                         uint16_t* out, float* lse, hipStream_t stream);
 
+// Gather-only measurement kernel (smla_gather_rows_probe).
+int64_t gather_probe_max_rows();
+hipError_t launch_gather_probe(const uint8_t* cache, int64_t num_slots, int rope_dim, const int32_t* slots,
+                               int64_t n, uint32_t* sink, hipStream_t stream);
+
 // Scratch of the allocation-free attention entry point: a device array of
 // kNoallocScratchBytes per GPU; *out = its address on the stream's device.
 constexpr size_t kNoallocScratchBytes = size_t(16) << 20;

@@ -10,6 +10,7 @@
 #include <cstring>
 
 #include "../include/sparse_mla.h"
+#include "../include/sparse_mla_measure.h"
 #include "../sparse_mla_attention_fp8_amd/csrc/common.h"
 
 static int g_launches = 0;
@@ -37,6 +38,10 @@ hipError_t launch_gather_upconvert(const uint8_t*, int64_t, int, const int64_t*,
 hipError_t launch_split_pages(const uint8_t*, int64_t, int64_t, const int32_t*, int64_t, uint8_t*, int64_t, int,
                               hipStream_t) { ++g_launches; return g_result; }
 hipError_t launch_merge(const uint16_t*, const float*, int, int64_t, uint16_t*, float*, hipStream_t) {
+  ++g_launches; return g_result;
+}
+int64_t gather_probe_max_rows() { return 256 * 8192; }
+hipError_t launch_gather_probe(const uint8_t*, int64_t, int, const int32_t*, int64_t, uint32_t*, hipStream_t) {
   ++g_launches; return g_result;
 }
 alignas(256) static unsigned char g_scratch_stub[256];
@@ -180,6 +185,15 @@ int main() {
   expect("pages row bytes", mla_split_pages_64(P, 8, INT64_MAX, idx, 4, Q, 64 * 656, INT_MAX - 15, s),
          SMLA_EINVAL);
   expect("pages stride", mla_split_pages_64(P, 8, INT64_MIN, idx, 4, Q, 64 * 656, 656, s), SMLA_EINVAL);
+
+  auto* sink = reinterpret_cast<uint32_t*>(buf + 1024);
+  expect("probe ok", smla_gather_rows_probe(P, 4096, 0, idx, 1000, sink, s), SMLA_OK);
+  expect("probe 0 rows", smla_gather_rows_probe(nullptr, 4096, 64, nullptr, 0, nullptr, s), SMLA_OK, true);
+  expect("probe max", smla_gather_rows_probe(P, 4096, 64, idx, INT64_MAX, sink, s), SMLA_EUNSUPPORTED);
+  expect("probe neg", smla_gather_rows_probe(P, 4096, 64, idx, -1, sink, s), SMLA_EINVAL);
+  expect("probe rope", smla_gather_rows_probe(P, 4096, 8, idx, 10, sink, s), SMLA_EINVAL);
+  expect("probe sink", smla_gather_rows_probe(P, 4096, 0, idx, 10, nullptr, s), SMLA_EINVAL);
+  expect("probe align", smla_gather_rows_probe(odd, 4096, 0, idx, 10, sink, s), SMLA_EINVAL);
 
   std::printf("%d cases, %d failed\n", g_cases, g_fail);
   return g_fail == 0 ? 0 : 1;
