@@ -98,6 +98,21 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
   return (uint32_t)(uintptr_t)(const lds_u8*)p;
 }
 
+// LDS pointer to byte a of the workgroup's LDS, for reads whose per-lane part
+// is fixed and whose stage part is a scalar: the compiler then folds every
+// constant offset into the instruction's offset field.
+__device__ __forceinline__ const lds_u8* lds_at(uint32_t a) {
+  return (const lds_u8*)(uintptr_t)a;
+}
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// (native vector and scalar types only: HIP's vector structs cannot be copied
+// from an LDS-qualified reference)
+template <typename T>
+__device__ __forceinline__ T lds_load(const lds_u8* p) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) T*>(p);
+}
+
 // 16 bytes per lane from global memory straight into LDS at lds_base + 16 * lane.
 // Issued as inline asm so the compiler adds no waits of its own for it: the
 // pipeline below accounts for these loads with explicit vmcnt waits.  m0 (the
@@ -440,36 +455,49 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void attn_mfma_kern
   // 2ps and 2ps + 1).
   long va[2][8];
   float sc[2][8];
-  auto read_pv = [&](const uint8_t* stg, long* v, float* s) {
-    const uint8_t* vsrc = stg + key_row(2 * ps + (k8 >> 2), 4 * g + (k8 & 3)) * RB + 128 * pt + 8 * h8;
+  // per-lane byte offsets of the P.V operand reads within a stage
+  const uint32_t pv_off = key_row(2 * ps + (k8 >> 2), 4 * g + (k8 & 3)) * RB + 128 * pt + 8 * h8;
+  const uint32_t sc_off0 = key_row(2 * ps, 4 * g) * RB + kScaleOff + 4 * pt;
+  const uint32_t sc_off1 = key_row(2 * ps + 1, 4 * g) * RB + kScaleOff + 4 * pt;
+  // stg: the stage's LDS address (wave-uniform)
+  auto read_pv = [&](uint32_t stg, long* v, float* s) {
+    const lds_u8* vsrc = lds_at(stg + pv_off);
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc) {
       const v2i tv = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(vsrc + 16 * cc));
       v[cc] = pack64((uint32_t)tv[0], (uint32_t)tv[1]);
     }
+    // slots 4bb..4bb+3 are four consecutive LDS rows
+    const lds_u8* srow0 = lds_at(stg + sc_off0);
+    const lds_u8* srow1 = lds_at(stg + sc_off1);
 #pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
-      // slots 4bb..4bb+3 are four consecutive LDS rows
-      const uint8_t* srow = stg + key_row(2 * ps + bb, 4 * g) * RB + kScaleOff + 4 * pt;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) s[4 * bb + r] = *reinterpret_cast<const float*>(srow + r * RB);
+    for (int r = 0; r < 4; ++r) {
+      s[r] = lds_load<float>(srow0 + r * RB);
+      s[4 + r] = lds_load<float>(srow1 + r * RB);
     }
   };
   // QK^T partial of a chunk: keys 16qb + [0,16), dims half qh.  The products
   // are issued early and combined late, so nothing waits on them in between.
   struct QkLoad { i8v a0, a1; bf16x8 ar; float2 sq[4]; };
   struct QkPart { f4 acc0, acc1, accr; float2 sq[4]; };
-  auto qk_load = [&](const uint8_t* stg) {
-    QkLoad o;
-    const uint8_t* krow = stg + key_row(qb, n16) * RB;
-    const uint4 p00 = *reinterpret_cast<const uint4*>(krow + 256 * qh + 32 * g);
-    const uint4 p01 = *reinterpret_cast<const uint4*>(krow + 256 * qh + 32 * g + 16);
-    const uint4 p10 = *reinterpret_cast<const uint4*>(krow + 256 * qh + 128 + 32 * g);
-    const uint4 p11 = *reinterpret_cast<const uint4*>(krow + 256 * qh + 128 + 32 * g + 16);
-    if (ROPE) o.ar = *reinterpret_cast<const bf16x8*>(krow + kRopeOff + 64 * qh + 16 * g);
+  const uint32_t k_off = key_row(qb, n16) * RB + 256 * qh + 32 * g;
+  const uint32_t kpe_off = key_row(qb, n16) * RB + kRopeOff + 64 * qh + 16 * g;
+  uint32_t sq_off[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      o.sq[r] = *reinterpret_cast<const float2*>(stg + key_row(qb, 4 * g + r) * RB + kScaleOff + 8 * qh);
+  for (int r = 0; r < 4; ++r) sq_off[r] = key_row(qb, 4 * g + r) * RB + kScaleOff + 8 * qh;
+  auto qk_load = [&](uint32_t stg) {
+    QkLoad o;
+    const lds_u8* krow = lds_at(stg + k_off);
+    const u32x4 p00 = lds_load<u32x4>(krow);
+    const u32x4 p01 = lds_load<u32x4>(krow + 16);
+    const u32x4 p10 = lds_load<u32x4>(krow + 128);
+    const u32x4 p11 = lds_load<u32x4>(krow + 128 + 16);
+    if (ROPE) o.ar = lds_load<bf16x8>(lds_at(stg + kpe_off));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const f32x2 v = lds_load<f32x2>(lds_at(stg + sq_off[r]));
+      o.sq[r] = make_float2(v.x, v.y);
+    }
     o.a0 = i8v{(int)p00.x, (int)p00.y, (int)p00.z, (int)p00.w, (int)p01.x, (int)p01.y, (int)p01.z, (int)p01.w};
     o.a1 = i8v{(int)p10.x, (int)p10.y, (int)p10.z, (int)p10.w, (int)p11.x, (int)p11.y, (int)p11.z, (int)p11.w};
     return o;
@@ -590,8 +618,8 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void attn_mfma_kern
       issue(lds0 + (uint32_t)((G::NST - 1) * G::STAGE), G::NST - 1);
     }
     if (G::NST < nch) fetch_slots(G::NST);
-    qk_finish(qk_mfma(qk_load(stages)), 0);
-    read_pv(stages, va[0], sc[0]);
+    qk_finish(qk_mfma(qk_load(lds0)), 0);
+    read_pv(lds0, va[0], sc[0]);
   }
   // One chunk; its P.V operands are in (vc, scc), the next chunk's go to
   // (vn, scn).  The loop runs two chunks per trip with the buffers swapped, so
@@ -616,7 +644,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void attn_mfma_kern
     if (c + G::NST < nch) issue(lds0 + (uint32_t)(cur * G::STAGE), c + G::NST);
 
     // ---- next chunk's operands (for the last chunk: stale bytes, results unused) ----
-    const uint8_t* nstg = stages + ((c + 1) % G::NST) * G::STAGE;
+    // (the stage address as an opaque scalar, so that the compiler keeps one
+    // base per read instead of one induction variable per address)
+    const uint32_t nstg = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(((c + 1) % G::NST) * G::STAGE));
     const QkLoad nk = qk_load(nstg);
     read_pv(nstg, vn, scn);
     if (c + G::NST + 1 < nch) fetch_slots(c + G::NST + 1);
