@@ -10,14 +10,18 @@
 // per (split, query row, group of 16 heads).  A split owns an equal share of
 // the row's valid entries (or, for a buffer wider than one scan, a fixed range
 // of it); the workgroup compacts its entries into LDS in buffer order and
-// walks them in chunks of 64 keys:
+// walks them in chunks of 64 keys.  Batches with more (row, head group) units
+// than one round of these workgroups run four-wavefront workgroups on 32-key
+// chunks instead, two per CU (see Geo):
 //
 //   gather  Each chunk's 64 rows (656 B, or the 528 B a NoPE reader needs)
 //           are copied HBM -> LDS with direct-to-LDS 16-byte loads, once per
-//           chunk and shared by all heads, into a ring of 3 (RoPE) or 4
-//           (NoPE) stages.  Below 4 GiB of cache the loads take a scalar
-//           base and a 32-bit per-lane offset (one 24-bit multiply-add per
-//           load); larger caches use 64-bit per-lane addresses.
+//           chunk and shared by all heads, into a ring of 3 stages.  Each
+//           wavefront issues a contiguous run of the chunk's 1-KB loads, four
+//           per m0 value through the loads' instruction offsets.  Below 4 GiB
+//           of cache the loads take a scalar base and a 32-bit per-lane
+//           offset (one 24-bit multiply-add per load); larger caches use
+//           64-bit per-lane addresses.
 //           Entries past the valid count of the last chunk get a copy of the
 //           chunk's first valid row (so every LDS operand is finite) and a
 //           weight that is exactly zero.
@@ -41,8 +45,8 @@
 // LDS) while it runs softmax and P.V on chunk c, whose V^T operands and tile
 // scales each P.V wavefront already holds in registers (read one iteration
 // earlier).  One workgroup barrier per chunk then both publishes the partial
-// scores and releases chunk c's stage, which is refilled at once, so three
-// chunks (NoPE) or two (RoPE) stay in flight while a chunk computes.
+// scores and releases chunk c's stage, which is refilled at once, so two
+// chunks stay in flight while a chunk computes.
 //
 // The key halves merge through LDS at the end.  With one split the workgroup
 // writes the bf16 output and LSE; with several it writes (O unnormalised fp32,
@@ -113,10 +117,79 @@ __device__ __forceinline__ T lds_load(const lds_u8* p) {
   return *reinterpret_cast<const __attribute__((address_space(3))) T*>(p);
 }
 
-// 16 bytes per lane from global memory straight into LDS at lds_base + 16 * lane.
-// Issued as inline asm so the compiler adds no waits of its own for it: the
-// pipeline below accounts for these loads with explicit vmcnt waits.  m0 (the
-// LDS base operand) is saved and restored around the load.
+// Direct-to-LDS gather loads (16 bytes per lane), issued as inline asm so the
+// compiler adds no waits of its own for them: the pipeline below accounts for
+// them with explicit vmcnt waits.  Lane l of a load writes LDS at m0 +
+// instruction offset + 16 l; the instruction offset is added to the global
+// address too, so callers take it off the per-lane address.  m0 is set from
+// two scalars (so the LDS address costs no vector instruction) and restored.
+//
+// Loads 0..3 of a wavefront: m0 = stage + wave_lds, offsets 0, 1024, 2048, 3072.
+// Either a scalar 64-bit base plus 32-bit per-lane offsets (caches below
+// 4 GiB) or 64-bit per-lane addresses.
+__device__ __forceinline__ void dma16x4(const uint8_t* base, uint32_t o0, uint32_t o1, uint32_t o2,
+                                        uint32_t o3, uint32_t stage, uint32_t wave_lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_add_u32 m0, %1, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %3, %7\n\t"
+      "global_load_lds_dwordx4 %4, %7 offset:1024\n\t"
+      "global_load_lds_dwordx4 %5, %7 offset:2048\n\t"
+      "global_load_lds_dwordx4 %6, %7 offset:3072\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(stage), "s"(wave_lds), "v"(o0), "v"(o1), "v"(o2), "v"(o3), "s"(base)
+      : "memory", "scc");
+}
+__device__ __forceinline__ void dma16x4(const uint8_t*, const uint8_t* p0, const uint8_t* p1,
+                                        const uint8_t* p2, const uint8_t* p3, uint32_t stage,
+                                        uint32_t wave_lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_add_u32 m0, %1, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %3, off\n\t"
+      "global_load_lds_dwordx4 %4, off offset:1024\n\t"
+      "global_load_lds_dwordx4 %5, off offset:2048\n\t"
+      "global_load_lds_dwordx4 %6, off offset:3072\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(stage), "s"(wave_lds), "v"(p0), "v"(p1), "v"(p2), "v"(p3)
+      : "memory", "scc");
+}
+// Load 4 + K of a wavefront: m0 = stage + wave_lds + 4096, offset 1024 K.
+template <int K>
+__device__ __forceinline__ void dma16_hi(const uint8_t* base, uint32_t o, uint32_t stage, uint32_t wave_lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_add_u32 m0, %1, %2\n\t"
+      "s_add_u32 m0, m0, 4096\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %3, %4 offset:%5\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(stage), "s"(wave_lds), "v"(o), "s"(base), "i"(1024 * K)
+      : "memory", "scc");
+}
+template <int K>
+__device__ __forceinline__ void dma16_hi(const uint8_t*, const uint8_t* p, uint32_t stage, uint32_t wave_lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_add_u32 m0, %1, %2\n\t"
+      "s_add_u32 m0, m0, 4096\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %3, off offset:%4\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(stage), "s"(wave_lds), "v"(p), "i"(1024 * K)
+      : "memory", "scc");
+}
+// q rows: 16 bytes per lane to lds_base + 16 * lane (m0 saved and restored).
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
   uint32_t saved;
   asm volatile(
@@ -130,8 +203,7 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
       : "memory");
 }
 
-// The same load with a scalar 64-bit base and a 32-bit per-lane byte offset
-// (caches below 4 GiB): the address needs no 64-bit arithmetic per lane.
+// The same with a scalar 64-bit base and a 32-bit per-lane byte offset.
 __device__ __forceinline__ void dma16_sbase(const uint8_t* base, uint32_t off, uint32_t lds_base) {
   uint32_t saved;
   asm volatile(
@@ -144,6 +216,30 @@ __device__ __forceinline__ void dma16_sbase(const uint8_t* base, uint32_t off, u
       : "v"(off), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds_base))
       : "memory");
 }
+
+// Load split of a chunk's NI loads over WAVES wavefronts (see the gather
+// geometry in attn_mfma_kernel): CNT1 = NI / WAVES each, one more for the last
+// R = NI % WAVES.  all_full(j): load j of every wavefront that issues it lies
+// wholly inside the chunk's SEGS segments.
+template <int NI, int WAVES, int SEGS>
+struct GatherGeo {
+  static constexpr int R = NI % WAVES;
+  static constexpr int CNT1 = NI / WAVES;
+  static constexpr int CNT0 = CNT1 + (R ? 1 : 0);
+  static constexpr bool all_full(int j) {
+    for (int w = 0; w < WAVES; ++w) {
+      const int cnt = CNT1 + (w >= WAVES - R ? 1 : 0);
+      const int start = w * CNT1 + (w - (WAVES - R) > 0 ? w - (WAVES - R) : 0);
+      if (j < cnt && 64 * (start + j + 1) > SEGS) return false;
+    }
+    return true;
+  }
+  static_assert(CNT1 >= 4 && CNT0 <= 8, "loads 0..3 of every wavefront share one m0, 4..7 another");
+  static_assert(all_full(0) && all_full(1) && all_full(2) && all_full(3), "loads 0..3 must be whole");
+};
+// The scalar base of the 32-bit gather offsets sits this far below the cache,
+// so that offsets stay non-negative after the instruction offset is taken off.
+constexpr uint32_t kGatherBias = 4096;
 
 // All waves' LDS writes visible to every wave of the workgroup (no wait on global loads).
 __device__ __forceinline__ void lds_barrier() {
@@ -162,11 +258,12 @@ __device__ __forceinline__ void vm_barrier() {
   compiler_fence();
 }
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0;
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// Two floats -> packed bf16 pair (low half = a), round to nearest even, by
+// the hardware conversion (v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  const bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ float exp2_pow(int e) {  // 2^e for e in [-126, 127]
@@ -384,24 +481,37 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void attn_mfma_kern
   float qs;
   bf16x8 qpe;
 
-  // ---- gather geometry: instruction i = wave + WAVES j covers flat segments
-  // 64i + lane of the chunk (a 32-key chunk ends halfway through its last
-  // instruction, whose upper 32 lanes load nothing)
-  constexpr int CNT0 = (G::NI + kWaves - 1) / kWaves;
-  constexpr int CNT1 = G::NI / kWaves;
-  const bool big = wave < G::NI % kWaves;        // issues CNT0 instructions, else CNT1
-  constexpr bool kWholeInstr = (kKeys * G::NSEG) % 64 == 0;   // no lane of an instruction idles
+  // ---- gather geometry.  A chunk is NI 1-KB direct-to-LDS loads; lane l of
+  // load i takes flat segment 64i + l of the chunk (a 32-key chunk ends halfway
+  // through its last load, whose upper 32 lanes load nothing).  Wavefront w
+  // issues loads [gstart, gstart + my_cnt): NI / WAVES each, the NI % WAVES
+  // left over going one each to the last wavefronts, so that the partial load
+  // is a wavefront's extra one.  Load j of a wavefront writes LDS block
+  // gstart + j of the stage: m0 = stage + 1024 gstart serves loads 0..3 through
+  // the instruction offset 1024 j, and m0 + 4096 the rest (1024 (j - 4)).
+  using GG = GatherGeo<G::NI, kWaves, kKeys * G::NSEG>;
+  constexpr int CNT0 = GG::CNT0;
+  constexpr int CNT1 = GG::CNT1;
+  const bool big = wave >= kWaves - GG::R;        // issues CNT0 loads, else CNT1
   const int my_cnt = big ? CNT0 : CNT1;
-  // row and byte offset of each of this lane's segments (fixed for the kernel)
+  const int gstart = wave * CNT1 + max(0, wave - (kWaves - GG::R));
+  // row and per-lane address part of each of this lane's segments (fixed for
+  // the kernel).  The instruction offset is added to the global address as
+  // well, so it is taken off here; with a 32-bit offset from a scalar base the
+  // base is moved down by kGatherBias bytes and the offset up, so the offset
+  // stays non-negative.
   int seg_row[CNT0], seg_off[CNT0];
   bool seg_ok[CNT0];
 #pragma unroll
   for (int j = 0; j < CNT0; ++j) {
-    const int f = 64 * (wave + kWaves * j) + lane;
-    seg_ok[j] = f < kKeys * G::NSEG;
+    const int f = 64 * (gstart + j) + lane;
+    seg_ok[j] = j < my_cnt && f < kKeys * G::NSEG;
     seg_row[j] = seg_ok[j] ? f / G::NSEG : 0;
-    seg_off[j] = seg_ok[j] ? (f - seg_row[j] * G::NSEG) * 16 : 0;
+    seg_off[j] = (seg_ok[j] ? (f - seg_row[j] * G::NSEG) * 16 : 0) - 1024 * (j & 3) +
+                 (SMALL ? kGatherBias : 0);
   }
+  const uint8_t* const gbase =
+      SMALL ? reinterpret_cast<const uint8_t*>(reinterpret_cast<uintptr_t>(cache) - kGatherBias) : cache;
   // Slots of the next chunk to gather, looked up one iteration ahead so that
   // the loads never wait on an LDS round trip (rows past the valid count take
   // the chunk's first row).
@@ -417,19 +527,34 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void attn_mfma_kern
       for (int j = 0; j < CNT0; ++j) slot[j] = slot_list[base + (seg_row[j] < nv ? seg_row[j] : 0)];
     }
   };
-  auto issue = [&](uint32_t stage, int c) {
+  // this wavefront's first 1-KB block of a stage (a scalar)
+  const uint32_t wave_lds = __builtin_amdgcn_readfirstlane(1024u * (uint32_t)gstart);
+  auto addr = [&](int j) {
+    if constexpr (SMALL) return __umul24((uint32_t)slot[j], (uint32_t)kRowBytes) + (uint32_t)seg_off[j];
+    else return cache + (int64_t)slot[j] * kRowBytes + seg_off[j];
+  };
+  auto issue = [&](uint32_t stage_in, int c) {
     (void)c;
-#pragma unroll
-    for (int j = 0; j < CNT0; ++j) {
-      if (j < my_cnt && (kWholeInstr || seg_ok[j])) {
-        const uint32_t lds = stage + 1024u * (uint32_t)(wave + kWaves * j);
-        if (SMALL) {
-          dma16_sbase(cache, __umul24((uint32_t)slot[j], (uint32_t)kRowBytes) + (uint32_t)seg_off[j], lds);
-        } else {
-          dma16(cache + (int64_t)slot[j] * kRowBytes + seg_off[j], lds);
+    const uint32_t stage = __builtin_amdgcn_readfirstlane(stage_in);
+    dma16x4(gbase, addr(0), addr(1), addr(2), addr(3), stage, wave_lds);
+    // loads 4..CNT0-1: a load that every wavefront issues and that lies wholly
+    // inside the chunk needs no per-lane condition (and no exec-mask branch)
+    auto hi = [&](auto kc) {
+      constexpr int K = decltype(kc)::value, j = 4 + K;
+      if constexpr (j < CNT0) {
+        if constexpr (j < CNT1 && GG::all_full(j)) {
+          dma16_hi<K>(gbase, addr(j), stage, wave_lds);
+        } else if constexpr (GG::all_full(j)) {
+          if (big) dma16_hi<K>(gbase, addr(j), stage, wave_lds);       // a scalar branch
+        } else if (seg_ok[j]) {
+          dma16_hi<K>(gbase, addr(j), stage, wave_lds);
         }
       }
-    }
+    };
+    hi(std::integral_constant<int, 0>{});
+    hi(std::integral_constant<int, 1>{});
+    hi(std::integral_constant<int, 2>{});
+    hi(std::integral_constant<int, 3>{});
   };
 
   // running max (log2 units) of this key half, per head; a finite sentinel
@@ -482,9 +607,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void attn_mfma_kern
   struct QkPart { f4 acc0, acc1, accr; float2 sq[4]; };
   const uint32_t k_off = key_row(qb, n16) * RB + 256 * qh + 32 * g;
   const uint32_t kpe_off = key_row(qb, n16) * RB + kRopeOff + 64 * qh + 16 * g;
-  uint32_t sq_off[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) sq_off[r] = key_row(qb, 4 * g + r) * RB + kScaleOff + 8 * qh;
+  // rows 4g..4g+3 of a block are consecutive LDS rows (key_row adds r to a
+  // multiple of 4 below 16), so one base serves all four
+  const uint32_t sq_off = key_row(qb, 4 * g) * RB + kScaleOff + 8 * qh;
   auto qk_load = [&](uint32_t stg) {
     QkLoad o;
     const lds_u8* krow = lds_at(stg + k_off);
@@ -495,7 +620,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void attn_mfma_kern
     if (ROPE) o.ar = lds_load<bf16x8>(lds_at(stg + kpe_off));
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const f32x2 v = lds_load<f32x2>(lds_at(stg + sq_off[r]));
+      const f32x2 v = lds_load<f32x2>(lds_at(stg + sq_off) + r * RB);
       o.sq[r] = make_float2(v.x, v.y);
     }
     o.a0 = i8v{(int)p00.x, (int)p00.y, (int)p00.z, (int)p00.w, (int)p01.x, (int)p01.y, (int)p01.z, (int)p01.w};
@@ -793,11 +918,8 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void attn_mfma_kern
       const float4 u = other_half(cc);
       const float o4[4] = {w0 * oacc[cc][0] + w1 * u.x, w0 * oacc[cc][1] + w1 * u.y,
                            w0 * oacc[cc][2] + w1 * u.z, w0 * oacc[cc][3] + w1 * u.w};
-      const uint32_t lo2 = (uint32_t)f32_to_bf16_rne(o4[0] * il) |
-                           ((uint32_t)f32_to_bf16_rne(o4[1] * il) << 16);
-      const uint32_t hi2 = (uint32_t)f32_to_bf16_rne(o4[2] * il) |
-                           ((uint32_t)f32_to_bf16_rne(o4[3] * il) << 16);
-      *reinterpret_cast<uint2*>(dst + 16 * cc) = make_uint2(lo2, hi2);
+      *reinterpret_cast<uint2*>(dst + 16 * cc) =
+          make_uint2(bf16x2_rne(o4[0] * il, o4[1] * il), bf16x2_rne(o4[2] * il, o4[3] * il));
     }
     if (lse != nullptr && pt == 0 && g == 0)
       lse[(int64_t)t * H + head] = L > 0.0f ? (M + __log2f(L)) * kLn2 : -INFINITY;
@@ -1121,8 +1243,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
       const float4 u = mo[cc * 256 + slot4];
       const float o4[4] = {w0 * oacc[cc][0] + w1 * u.x, w0 * oacc[cc][1] + w1 * u.y,
                            w0 * oacc[cc][2] + w1 * u.z, w0 * oacc[cc][3] + w1 * u.w};
-      const uint32_t lo2 = (uint32_t)f32_to_bf16_rne(o4[0] * il) | ((uint32_t)f32_to_bf16_rne(o4[1] * il) << 16);
-      const uint32_t hi2 = (uint32_t)f32_to_bf16_rne(o4[2] * il) | ((uint32_t)f32_to_bf16_rne(o4[3] * il) << 16);
+      const uint32_t lo2 = bf16x2_rne(o4[0] * il, o4[1] * il);
+      const uint32_t hi2 = bf16x2_rne(o4[2] * il, o4[3] * il);
       *reinterpret_cast<uint2*>(dst + 16 * cc) = make_uint2(lo2, hi2);
     }
     if (lse != nullptr && pt == 0 && g == 0)
@@ -1223,7 +1345,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void attn_merge_kernel(const floa
   uint32_t pk[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    pk[i] = (uint32_t)f32_to_bf16_rne(o[2 * i] * inv) | ((uint32_t)f32_to_bf16_rne(o[2 * i + 1] * inv) << 16);
+    pk[i] = bf16x2_rne(o[2 * i] * inv, o[2 * i + 1] * inv);
   *reinterpret_cast<uint4*>(out + (int64_t)th * kLatent + 8 * lane) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
   if (lse != nullptr && lane == 0) lse[th] = (Lt > 0.0f) ? (M + __log2f(Lt)) * kLn2 : -INFINITY;
 }
@@ -1284,7 +1406,7 @@ __global__ __launch_bounds__(64 * kMergeSmallRows) void attn_merge_small_kernel(
   uint32_t pk[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    pk[i] = (uint32_t)f32_to_bf16_rne(acc[2 * i] * inv) | ((uint32_t)f32_to_bf16_rne(acc[2 * i + 1] * inv) << 16);
+    pk[i] = bf16x2_rne(acc[2 * i] * inv, acc[2 * i + 1] * inv);
   *reinterpret_cast<uint4*>(out + (int64_t)th * kLatent + 8 * lane) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
   if (lse != nullptr && lane == 0) lse[th] = (L > 0.0f) ? (M + __log2f(L)) * kLn2 : -INFINITY;
 }
@@ -1318,7 +1440,8 @@ hipError_t launch_attn(const uint16_t* q, const uint8_t* cache, int64_t num_slot
   const int64_t blocks = plan.blocks;
   const float sl2 = sm_scale * kLog2e;
   // row byte offsets fit 32 bits (and slot * 656 fits the 24-bit multiply)
-  const bool small = num_slots <= (int64_t)(0xFFFFFFFFull / kRowBytes) && num_slots < (1 << 24);
+  const bool small = num_slots <= (int64_t)((0xFFFFFFFFull - 2 * kGatherBias) / kRowBytes) &&
+                     num_slots < (1 << 24);
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(64 * plan.waves), 0, stream, q, cache,
                        num_slots, idx, idx_stride, W, H, sl2, plan.range, plan.splits, plan.head_groups,

@@ -255,6 +255,54 @@ def test_cache_beyond_4_gib(rope_dim):
     assert_parity(out, lse, ref_out, ref_lse, range(T))
 
 
+# The largest cache the 32-bit gather path takes (its scalar base sits 4 KiB
+# below the cache and 8 KiB of offset range stay free); one slot more takes the
+# 64-bit path.
+LARGEST_32BIT_SLOTS = (0xFFFFFFFF - 8192) // wl.ROW_BYTES
+
+
+@pytest.mark.parametrize("T", [4, 300])
+@pytest.mark.parametrize("rope_dim", [0, 64])
+def test_largest_32bit_cache_and_lowest_slots(rope_dim, T):
+    """The last slots of the largest cache the 32-bit gather path takes, and
+    slots 1..6 (row offsets below the 4 KiB that the loads' instruction
+    offsets reach), in every row; 4 rows run eight-wavefront workgroups, 300
+    rows four-wavefront ones."""
+    from oracle import attention as oracle_attn
+    from oracle import writer as oracle_writer
+    print(f"largest 32-bit cache rope={rope_dim} T={T}", flush=True)
+    num_slots = LARGEST_32BIT_SLOTS
+    assert (num_slots + 1) * wl.ROW_BYTES > 0xFFFFFFFF - 8192
+    rng = np.random.default_rng(860 + rope_dim + T)
+    H, W = 16, 160
+    idx = np.full((T, W), -1, dtype=np.int32)
+    for t in range(T):
+        n = 6 + 1 + (t * 37) % (W - 7)
+        v = np.concatenate([np.arange(1, 7), [num_slots - 1],
+                            rng.choice(np.arange(num_slots - 4000, num_slots - 1), size=n - 7, replace=False)])
+        rng.shuffle(v)
+        idx[t, :n] = v
+    slots = np.unique(idx[idx >= 0]).astype(np.int64)
+    latent = wl.normal_bf16(rng, (slots.size, 512))
+    rope = wl.normal_bf16(rng, (slots.size, rope_dim)) if rope_dim else None
+    cache = torch.empty((num_slots, wl.ROW_BYTES), dtype=torch.uint8, device=DEV)
+    cache[0] = 0x7F
+    lat_d = torch.from_numpy(latent.view(np.int16)).view(torch.bfloat16).to(DEV)
+    rope_d = torch.from_numpy(rope.view(np.int16)).view(torch.bfloat16).to(DEV) if rope_dim else None
+    smla.kv_write(lat_d, rope_d, torch.from_numpy(slots).to(DEV), cache)
+    q = wl.normal_bf16(rng, (T, H, 512 + rope_dim))
+    sm = float(1.0 / np.sqrt(512 + rope_dim))
+    out, lse = smla.attn(torch.from_numpy(q.view(np.int16)).view(torch.bfloat16).to(DEV), cache,
+                         torch.from_numpy(idx).to(DEV), sm, rope_dim)
+    torch.cuda.synchronize()
+    host = np.zeros((num_slots, wl.ROW_BYTES), dtype=np.uint8)
+    host[slots] = oracle_writer.encode_rows(latent, rope)
+    host[0] = 0x7F
+    ref_out, ref_lse = oracle_attn.sparse_mla_attn(q, host, idx, W, rope_dim, sm)
+    del cache
+    assert_parity(out, lse, ref_out, ref_lse, range(T))
+
+
 def test_buffer_wider_than_one_scan():
     """A top-k buffer wider than one split's scan (3,000 > 2,304 entries): the
     row is cut into fixed ranges instead of dealt out; valid entries and -1
