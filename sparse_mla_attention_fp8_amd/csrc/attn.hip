@@ -516,15 +516,19 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void attn_mfma_kern
   // the loads never wait on an LDS round trip (rows past the valid count take
   // the chunk's first row).
   int slot[CNT0];
+  const uint32_t list0 = lds_addr(reinterpret_cast<const uint8_t*>(slot_list));
   auto fetch_slots = [&](int c) {
     const int base = c * kKeys;
     const int nv = min(kKeys, n - base);
-    if (nv == kKeys) {
+    const uint32_t cb = list0 + 4u * (uint32_t)base;      // the chunk's entries (a scalar)
+    // (a chunk's positions lie within the list, so the rows past the valid
+    // count read stale entries that are replaced below)
 #pragma unroll
-      for (int j = 0; j < CNT0; ++j) slot[j] = slot_list[base + seg_row[j]];
-    } else {
+    for (int j = 0; j < CNT0; ++j) slot[j] = lds_load<int>(lds_at(cb + 4u * (uint32_t)seg_row[j]));
+    if (nv < kKeys) {
+      const int first = lds_load<int>(lds_at(cb));
 #pragma unroll
-      for (int j = 0; j < CNT0; ++j) slot[j] = slot_list[base + (seg_row[j] < nv ? seg_row[j] : 0)];
+      for (int j = 0; j < CNT0; ++j) slot[j] = seg_row[j] < nv ? slot[j] : first;
     }
   };
   // this wavefront's first 1-KB block of a stage (a scalar)
@@ -869,8 +873,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void attn_mfma_kern
   };
   for (int c = 0; c < nch; c += 2) {
     step(c, va[0], sc[0], va[1], sc[1]);
-    if (c + 1 >= nch) break;
-    step(c + 1, va[1], sc[1], va[0], sc[0]);
+    if (c + 1 < nch) step(c + 1, va[1], sc[1], va[0], sc[0]);
   }
 
   // ---- combine the two key halves (eight wavefronts), then write ------------
