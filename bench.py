@@ -342,6 +342,9 @@ def main():
         "gathered_bytes_per_step": bytes_step,
         "unique_row_bytes_per_step": int(np.unique(cfg["idx"][cfg["idx"] >= 0]).size) * NOPE_ROW,
     }
+    # the three byte counts side by side, each over the attention launch's time:
+    # algorithmic (attn_gbs), distinct rows only, and counter-derived (below)
+    result["attn_unique_row_gbs"] = round(result["unique_row_bytes_per_step"] / (attn_us.mean() * 1e3), 1)
     result["roofline"] = {
         "bound": "hbm",
         "achieved": round(attn_gbs, 1),
@@ -354,6 +357,7 @@ def main():
     tr = measured_traffic()
     if tr is not None:
         result["roofline"]["traffic"] = tr["hbm_bytes_per_launch"]
+        result["attn_counter_gbs"] = round(tr["hbm_bytes_per_launch"] / (attn_us.mean() * 1e3), 1)
         result["roofline"]["traffic_detail"] = {k: tr[k] for k in
                                                 ("fetch_bytes_per_launch", "write_bytes_per_launch",
                                                  "copy_scale_fetch", "copy_scale_write")}
