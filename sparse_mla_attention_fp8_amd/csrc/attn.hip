@@ -656,8 +656,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void attn_mfma_kern
   };
 
   // ---- pipeline: chunk c lives in stage c % NST ----
-  // The first NST chunks are issued as soon as the index list is in LDS; q is
-  // split while they are in flight.  Every compiler-visible global load (the
+  // Chunk 0 is issued as soon as the index list is in LDS and q is split while
+  // it flies; chunk 1 follows, and the ring's last stage is filled once chunk
+  // 0 has landed.  Every compiler-visible global load (the
   // index scan's) has been consumed by then, so the compiler has no reason to
   // emit a vmcnt wait of its own in the loop (it does not count the inline-asm
   // gathers; a wait of its own there would drain the whole pipeline).
@@ -725,8 +726,11 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void attn_mfma_kern
     }
   }
   qpe = __builtin_bit_cast(bf16x8, qpe_raw);
-  // the other chunks of the ring, but not yet the stage that holds q
-  constexpr int kFirst = G::Q_IN_STAGE ? G::NST - 1 : G::NST;
+  // the other chunks of the ring but the last, which is issued once chunk 0
+  // has landed: chunk 0 then shares the memory system with one chunk per
+  // workgroup instead of two, and lands sooner (with four wavefronts that
+  // stage also holds q until every wavefront has split it)
+  constexpr int kFirst = G::NST - 1;
 #pragma unroll
   for (int c = 1; c < kFirst; ++c)
     if (c < nch) {
@@ -742,7 +746,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void attn_mfma_kern
     else if (ahead == 1) { if (big) vm_barrier<CNT0>(); else vm_barrier<CNT1>(); }
     else { if (big) vm_barrier<2 * CNT0>(); else vm_barrier<2 * CNT1>(); }
     // every wavefront has split q by now, so its stage can take its chunk
-    if (G::Q_IN_STAGE && G::NST - 1 < nch) {
+    if (G::NST - 1 < nch) {
       fetch_slots(G::NST - 1);
       issue(lds0 + (uint32_t)((G::NST - 1) * G::STAGE), G::NST - 1);
     }
