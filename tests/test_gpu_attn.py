@@ -387,7 +387,8 @@ def test_single_entry_rows_and_an_all_padding_batch():
 # ---- calls with more (row, head group) units than one round of eight-wavefront
 # workgroups run four-wavefront workgroups (32-key chunks, two per CU)
 
-@pytest.mark.parametrize("kind,T,H", [("nope", 300, 16), ("rope", 260, 32), ("rope", 257, 16)])
+@pytest.mark.parametrize("kind,T,H", [("nope", 300, 16), ("rope", 260, 32), ("rope", 257, 16),
+                                        ("nope", 140, 20)])
 def test_four_wave_decode_every_row(kind, T, H):
     print(f"four-wave {kind} T={T} H={H}", flush=True)
     if kind == "nope":
