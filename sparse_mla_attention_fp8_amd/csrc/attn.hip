@@ -887,14 +887,18 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void attn_mfma_kern
   for (int cc = 0; cc < 8; ++cc)
 #pragma unroll
     for (int r = 0; r < 4; ++r) oacc[cc][r] *= post;
-  float4* mo = reinterpret_cast<float4*>(stages);              // [c][pt][lane] partial O (32 KB)
-  float2* ml = reinterpret_cast<float2*>(stages + 4 * 64 * 128);  // [pt][lane] (m, l)
+  // The halves meet in buffers no wavefront can still be reading, so no
+  // barrier is needed before they are written: a wavefront still in the last
+  // iteration reads only stage nch % NST and the partial scores, so stage
+  // (nch + 1) % NST takes O and the index list (read no more) takes (m, l).
+  static_assert(WAVES != 8 || (4 * 64 * 128 <= G::STAGE && 256 * sizeof(float2) <= sizeof(slot_list)), "combine buffers");
+  float4* mo = reinterpret_cast<float4*>(stages + (uint32_t)(((nch + 1) % G::NST) * G::STAGE));   // [c][pt][lane] (32 KB)
+  float2* ml = reinterpret_cast<float2*>(slot_list);                                             // [pt][lane] (m, l)
   const int slot4 = pt * 64 + lane;
   // with four wavefronts every P.V wavefront holds the whole row of its tile:
   // its own state, weight 1, and nothing from another half
   float M = m_run, L = l_full, w0 = 1.0f, w1 = 0.0f;
   if constexpr (WAVES == 8) {
-    lds_barrier();                       // every wave is done with the stages
     if (ps == 1) {
 #pragma unroll
       for (int cc = 0; cc < 8; ++cc)
