@@ -72,3 +72,31 @@ def test_noalloc_refuses_plans_beyond_the_scratch():
     assert e.value.code == smla.SMLA_EWORKSPACE and "scratch" in str(e.value)
     torch.cuda.synchronize()
     assert bool((out == 7.0).all())               # nothing was launched
+
+
+def test_noalloc_in_a_graph():
+    """The call captured in a HIP graph (split plan and merge, T = 16): every
+    replay, with eager calls that use the same scratch between replays, gives
+    the workspace entry point's bytes."""
+    print("noalloc graph T=16", flush=True)
+    cfg = wl.config_nope_decode(16, seed=313, num_slots=16384, ctx=(512, 16384))
+    cache = build_cache(cfg)
+    T = 16
+    q = bf16_dev(cfg["q"])
+    idx = torch.from_numpy(cfg["idx"]).to(DEV)
+    ref_out, ref_lse = smla.attn(q, cache, idx, cfg["sm_scale"], 0)
+    out = torch.empty((T, cfg["H"], 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((T, cfg["H"]), dtype=torch.float32, device=DEV)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        smla.attn_noalloc(q, cache, idx, cfg["sm_scale"], 0, out, lse)
+    q_other = bf16_dev(wl.normal_bf16(np.random.default_rng(9), tuple(q.shape)))
+    o2 = torch.empty_like(out)
+    for rep in range(4):
+        smla.attn_noalloc(q_other, cache, idx, cfg["sm_scale"], 0, o2)   # same scratch, other partials
+        out.zero_()
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), f"replay {rep} differs"
