@@ -149,7 +149,10 @@ size_t sparse_mla_attn_workspace_size(int T, int H, int topk_capacity, int rope_
  * lse             float32 [T][H] natural-log LSE, or NULL.
  * workspace       device memory of >= sparse_mla_attn_workspace_size(T, H,
  *                 topk_capacity, rope_dim) bytes (16-byte aligned), or NULL
- *                 when that size is 0.  Its contents on entry do not matter.
+ *                 when that size is 0.  Its contents on entry do not matter
+ *                 (split partials, and with two or three splits per row the
+ *                 words that find the split finishing last, which each call
+ *                 leaves zero); two calls that share it must not overlap.
  */
 int sparse_mla_attn(const void* q,
                     const void* kv_cache, int64_t num_slots,

@@ -50,9 +50,16 @@
 //
 // The key halves merge through LDS at the end.  With one split the workgroup
 // writes the bf16 output and LSE; with several it writes (O unnormalised fp32,
-// m, l) partials that a merge kernel combines (attn_merge_small_kernel up to
-// 16 splits, attn_merge_kernel beyond).  m is kept in log2 units throughout.
+// m, l) partials.  With two or three splits (eight wavefronts) the split of a
+// row that finishes last merges them in the same launch: partials go through
+// device-coherent stores and loads, and an arrival word per (row, head group)
+// in the workspace names the last split.  Otherwise a merge kernel combines
+// them (attn_merge_small_kernel up to 16 splits, attn_merge_kernel beyond).
+// m is kept in log2 units throughout.
 #include "common.h"
+
+#include <atomic>
+#include <random>
 
 namespace smla {
 namespace {
@@ -393,6 +400,38 @@ __device__ int compact_valid(const int32_t* __restrict__ idx, int lo, int hi, in
   return w1 - w0;
 }
 
+// Device-coherent 16- and 8-byte accesses (cache policy sc1, device scope)
+// through a raw buffer resource: stores write through to the memory side and
+// loads miss any copy a cache holds, so a workgroup on one XCD reads what a
+// workgroup on another has stored once that one's stores have completed.
+constexpr int kBufWord3 = 0x00020000;     // raw buffer, 32-bit data format (gfx9 family)
+constexpr int kDeviceScope = 16;          // cache-policy operand: sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufWord3);
+}
+
+// Arrival of one split at its (row, head group) word; true for the split that
+// arrives last, which then leaves the word zero.  The word holds the call's
+// tag (epoch << 8) plus the splits arrived so far; a word with another tag (the
+// zero a finished call leaves, or whatever the workspace held) counts as none
+// arrived.  Each failed exchange is another split's arrival, so the loop ends
+// within `splits` tries.
+__device__ __noinline__ bool arrive_last(unsigned long long* word, unsigned long long epoch, int splits) {
+  const unsigned long long tag = epoch << 8;
+  unsigned long long old = 0;
+  int count = 0;
+  for (int i = 0; i <= kFusedMaxSplits; ++i) {
+    const unsigned long long want = ((old & ~0xFFull) == tag ? old : tag) + 1;
+    if (__hip_atomic_compare_exchange_strong(word, &old, want, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT)) {
+      count = (int)(want & 0xFF);
+      break;
+    }
+  }
+  if (count == splits) __hip_atomic_store(word, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return count == splits;
+}
+
 // SMALL: the cache spans less than 4 GiB, so row byte offsets fit 32 bits.
 // WAVES: 8 (one workgroup per CU) or 4 (two per CU), see Geo.
 template <int ROPE, bool SMALL, int WAVES>
@@ -400,7 +439,8 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void attn_mfma_kern
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ cache, int64_t num_slots,
     const int32_t* __restrict__ idx, int64_t idx_stride, int W, int H, float sm_scale_log2,
     int range, int splits, int head_groups, uint16_t* __restrict__ out, float* __restrict__ lse,
-    float* __restrict__ part_o, float* __restrict__ part_ml) {
+    float* __restrict__ part_o, float* __restrict__ part_ml, unsigned long long* __restrict__ arrive,
+    unsigned long long epoch) {
   using G = Geo<ROPE, WAVES>;
   constexpr int D = G::D, RB = G::RB;
   constexpr int kWaves = WAVES;
@@ -898,6 +938,8 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void attn_mfma_kern
   // with four wavefronts every P.V wavefront holds the whole row of its tile:
   // its own state, weight 1, and nothing from another half
   float M = m_run, L = l_full, w0 = 1.0f, w1 = 0.0f;
+  // a merge inside this launch needs every wavefront until the row is merged
+  const bool fused = WAVES == 8 && arrive != nullptr;
   if constexpr (WAVES == 8) {
     if (ps == 1) {
 #pragma unroll
@@ -906,13 +948,15 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void attn_mfma_kern
       ml[slot4] = make_float2(m_run, l_full);
     }
     lds_barrier();
-    if (ps == 1 || !hvalid) return;
-    const float2 o1 = ml[slot4];
-    M = fmaxf(m_run, o1.x);
-    // (a half without valid keys has l = 0, so its weight does not matter)
-    w0 = __builtin_amdgcn_exp2f(m_run - M);
-    w1 = __builtin_amdgcn_exp2f(o1.x - M);
-    L = w0 * l_full + w1 * o1.y;
+    if (!fused && (ps == 1 || !hvalid)) return;
+    if (ps == 0) {
+      const float2 o1 = ml[slot4];
+      M = fmaxf(m_run, o1.x);
+      // (a half without valid keys has l = 0, so its weight does not matter)
+      w0 = __builtin_amdgcn_exp2f(m_run - M);
+      w1 = __builtin_amdgcn_exp2f(o1.x - M);
+      L = w0 * l_full + w1 * o1.y;
+    }
   } else {
     if (!hvalid) return;
   }
@@ -934,7 +978,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void attn_mfma_kern
     }
     if (lse != nullptr && pt == 0 && g == 0)
       lse[(int64_t)t * H + head] = L > 0.0f ? (M + __log2f(L)) * kLn2 : -INFINITY;
-  } else {
+  } else if (!fused) {
     const int64_t pidx = ((int64_t)t * splits + split) * H + head;
     float* dst = part_o + pidx * kLatent + dim0;
 #pragma unroll
@@ -948,6 +992,85 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void attn_mfma_kern
       part_ml[2 * pidx] = M;
       part_ml[2 * pidx + 1] = L;
     }
+  } else if constexpr (WAVES == 8) {
+    // The row's partials, [split][head][512] and [split][head](m, l) from its
+    // first head, reached through device-coherent accesses: every split stores
+    // its own, and the split that arrives last reads them all back.
+    const int64_t row0 = (int64_t)t * splits * H;
+    const uint32_t o_bytes = (uint32_t)(splits * H * kLatent * 4);
+    const __amdgpu_buffer_rsrc_t ro = coherent_rsrc(part_o + row0 * kLatent, o_bytes);
+    const __amdgpu_buffer_rsrc_t rm = coherent_rsrc(part_ml + 2 * row0, (uint32_t)(splits * H * 8));
+    f4 mine[8];                            // this split's O at (head, dim0 + 16cc + r)
+    if (ps == 0 && hvalid) {
+      const uint32_t po = (uint32_t)(((split * H + head) * kLatent + dim0) * 4);
+#pragma unroll
+      for (int cc = 0; cc < 8; ++cc) {
+        const float4 u = other_half(cc);
+        mine[cc] = f4{w0 * oacc[cc][0] + w1 * u.x, w0 * oacc[cc][1] + w1 * u.y,
+                      w0 * oacc[cc][2] + w1 * u.z, w0 * oacc[cc][3] + w1 * u.w};
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, mine[cc]), ro, po + 64 * cc, 0,
+                                               kDeviceScope);
+      }
+      if (pt == 0 && g == 0) {
+        const v2i mlv = v2i{(int)__float_as_uint(M), (int)__float_as_uint(L)};
+        __builtin_amdgcn_raw_buffer_store_b64(mlv, rm, (uint32_t)((split * H + head) * 8), 0, kDeviceScope);
+      }
+    }
+    // every wavefront's stores have completed before the split arrives
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();
+    int* last = slot_list;                 // the index list is read no more
+    if (tid == 0) *last = arrive_last(arrive + (int64_t)t * head_groups + hg, epoch, splits) ? 1 : 0;
+    lds_barrier();
+    if (*last == 0) return;
+    // The last split merges the row where its own values already are: each
+    // writer lane combines its 32 outputs (head n16, dims dim0 + 16cc + r)
+    // over the splits in split order, its own from registers and the others'
+    // read back, with the merge kernels' arithmetic (M = max m_s, weights
+    // 2^(m_s - M), O = sum w_s O_s / sum w_s l_s).
+    if (ps == 1 || !hvalid) return;
+    float ms[kFusedMaxSplits], ls[kFusedMaxSplits];
+    f4 a[kFusedMaxSplits][8];
+#pragma unroll
+    for (int j = 0; j < kFusedMaxSplits; ++j) {
+      const bool load = j < splits && j != split;
+      const uint32_t hm = (uint32_t)(j * H + head);
+      const v2i mlv = load ? __builtin_amdgcn_raw_buffer_load_b64(rm, hm * 8, 0, kDeviceScope) : v2i{0, 0};
+      ms[j] = j == split ? M : (load ? __uint_as_float((uint32_t)mlv[0]) : -INFINITY);
+      ls[j] = j == split ? L : (load ? __uint_as_float((uint32_t)mlv[1]) : 0.0f);
+#pragma unroll
+      for (int cc = 0; cc < 8; ++cc)
+        a[j][cc] = load ? __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(
+                              ro, (hm * kLatent + dim0 + 16 * cc) * 4, 0, kDeviceScope))
+                        : f4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    float mg = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kFusedMaxSplits; ++j) mg = fmaxf(mg, ms[j]);
+    const float f0 = __builtin_amdgcn_exp2f(-INFINITY - mg);   // 0, as a merge kernel's first group
+    float Lm = 0.0f * f0;
+    f4 acc[8];
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) acc[cc] = f4{0.0f, 0.0f, 0.0f, 0.0f} * f0;
+#pragma unroll
+    for (int j = 0; j < kFusedMaxSplits; ++j) {
+      const float w = __builtin_amdgcn_exp2f(ms[j] - mg);   // 0 past the last split
+      Lm += w * ls[j];
+#pragma unroll
+      for (int cc = 0; cc < 8; ++cc) {
+        const f4 v = j == split ? mine[cc] : a[j][cc];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[cc][e] += w * v[e];
+      }
+    }
+    const float inv = (Lm > 0.0f) ? 1.0f / Lm : 0.0f;
+    const int64_t th = (int64_t)t * H + head;
+    uint16_t* dsto = out + th * kLatent + dim0;
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc)
+      *reinterpret_cast<uint2*>(dsto + 16 * cc) =
+          make_uint2(bf16x2_rne(acc[cc][0] * inv, acc[cc][1] * inv), bf16x2_rne(acc[cc][2] * inv, acc[cc][3] * inv));
+    if (lse != nullptr && pt == 0 && g == 0) lse[th] = (Lm > 0.0f) ? (mg + __log2f(Lm)) * kLn2 : -INFINITY;
   }
 }
 
@@ -1438,6 +1561,16 @@ hipError_t launch_merge(const float* part_o, const float* part_ml, int splits, i
 
 }  // namespace
 
+// Tags of fused-merge calls: distinct for every call of the process (below
+// 2^56), from a random start so that no leftover workspace word matches one.
+unsigned long long next_epoch() {
+  static std::atomic<unsigned long long> counter{[] {
+    std::random_device rd;
+    return ((((unsigned long long)rd() << 32) | rd()) >> 9) | 1ull;
+  }()};
+  return counter.fetch_add(1, std::memory_order_relaxed) % ((1ull << 56) - 1) + 1;
+}
+
 hipError_t launch_attn(const uint16_t* q, const uint8_t* cache, int64_t num_slots,
                        const int32_t* idx, int64_t idx_stride, int W, int T, int H,
                        int rope_dim, float sm_scale, uint16_t* out, float* lse,
@@ -1453,10 +1586,17 @@ hipError_t launch_attn(const uint16_t* q, const uint8_t* cache, int64_t num_slot
   // row byte offsets fit 32 bits (and slot * 656 fits the 24-bit multiply)
   const bool small = num_slots <= (int64_t)((0xFFFFFFFFull - 2 * kGatherBias) / kRowBytes) &&
                      num_slots < (1 << 24);
+  // the fused merge's arrival words, and a tag no earlier call used
+  unsigned long long* arrive = nullptr;
+  unsigned long long epoch = 0;
+  if (plan.fused) {
+    arrive = reinterpret_cast<unsigned long long*>(static_cast<uint8_t*>(workspace) + plan.arrive_off);
+    epoch = next_epoch();
+  }
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(64 * plan.waves), 0, stream, q, cache,
                        num_slots, idx, idx_stride, W, H, sl2, plan.range, plan.splits, plan.head_groups,
-                       out, lse, part_o, part_ml);
+                       out, lse, part_o, part_ml, arrive, epoch);
   };
   if (plan.waves == 4) {
     if (rope_dim == 64) {
@@ -1472,7 +1612,7 @@ hipError_t launch_attn(const uint16_t* q, const uint8_t* cache, int64_t num_slot
     }
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || plan.splits == 1) return e;
+  if (e != hipSuccess || plan.splits == 1 || plan.fused) return e;
   return launch_merge(part_o, part_ml, plan.splits, T, H, out, lse, stream);
 }
 

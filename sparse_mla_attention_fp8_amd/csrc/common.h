@@ -18,6 +18,7 @@ constexpr int kHeads = 16;          // heads per workgroup (MFMA N)
 constexpr int kKeys = 64;           // keys per chunk (4 blocks of 16)
 constexpr int kMaxRange = 2304;     // top-k entries one split may own (LDS index list)
 constexpr int kTargetBlocks = 256;  // one workgroup per CU (LDS-bound occupancy)
+constexpr int kFusedMaxSplits = 3;  // largest split count merged inside the main launch
 
 // Internal launchers (return a hipError_t from the launch).
 hipError_t launch_kv_write(const uint16_t* kv_c, int64_t kv_c_stride, const uint16_t* k_pe,
@@ -41,7 +42,11 @@ struct AttnPlan {
   int range;         // top-k entries per split (multiple of the chunk size); 0: every split
                      // scans the whole row and keeps an equal share of its valid entries
   int64_t blocks;    // workgroups of the main launch (splits * T * head_groups)
-  size_t workspace;  // bytes of partial results (0 when splits == 1)
+  int fused;         // 1: the split of a (row, head group) that finishes last merges the
+                     // row's partials inside the main launch (eight-wavefront plans of
+                     // 2..kFusedMaxSplits splits); 0: a merge kernel follows
+  size_t arrive_off; // byte offset in the workspace of the fused merge's arrival words
+  size_t workspace;  // bytes of partial results and arrival words (0 when splits == 1)
 };
 AttnPlan plan_attn(int T, int H, int topk_capacity, int rope_dim);
 

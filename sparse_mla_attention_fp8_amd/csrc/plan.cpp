@@ -35,7 +35,12 @@ AttnPlan plan_attn(int T, int H, int W, int rope_dim) {
   // and first gathers overlap the other's chunks
   p.waves = units > kTargetBlocks ? 4 : 8;
   p.blocks = s * units;
-  p.workspace = (s > 1) ? (size_t)T * (size_t)s * (size_t)H * (kLatent + 2) * sizeof(float) : 0;
+  // with a few splits the last one to finish merges its row: that costs two
+  // memory round trips instead of a second launch
+  p.fused = (p.waves == 8 && s > 1 && s <= kFusedMaxSplits) ? 1 : 0;
+  const size_t partials = (s > 1) ? (size_t)T * (size_t)s * (size_t)H * (kLatent + 2) * sizeof(float) : 0;
+  p.arrive_off = partials;     // a multiple of 8
+  p.workspace = partials + (p.fused ? (size_t)units * sizeof(unsigned long long) : 0);
   return p;
 }
 

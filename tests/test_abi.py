@@ -162,15 +162,20 @@ def test_split_pages_validation():
 def test_plan_fits_one_round_of_workgroups():
     """One workgroup runs per CU (256 on the chip), so the split count keeps a
     launch to one round of workgroups: 65 rows take 3 splits (195 workgroups),
-    not 4 (260, where 4 would wait for a second round)."""
+    not 4 (260, where 4 would wait for a second round).  Plans of two or three
+    splits merge inside the launch and add one 8-byte arrival word per
+    (row, head group) to the partials."""
     rec = 16 * 514 * 4
     for T in range(1, 300):
         ws = smla.workspace_size(T, 16, 2048, 64)
         s = ws // (rec * T) if ws else 1
-        assert ws == 0 or ws == s * rec * T
+        words = 8 * T if 2 <= s <= 3 else 0
+        assert ws == 0 or ws == s * rec * T + words
         assert s == 1 or s * T <= 256, (T, s)
         assert s <= 32                               # no more splits than 64-key chunks
-    assert smla.workspace_size(65, 16, 2048, 64) == 3 * rec * 65
+    assert smla.workspace_size(65, 16, 2048, 64) == 3 * rec * 65 + 8 * 65
+    assert smla.workspace_size(100, 16, 2176, 0) == 2 * rec * 100 + 8 * 100
+    assert smla.workspace_size(40, 32, 2176, 0) == 3 * (2 * rec) * 40 + 8 * 40 * 2
     assert smla.workspace_size(64, 16, 2176, 0) == 4 * rec * 64
     assert smla.workspace_size(257, 16, 2048, 64) == 0
 

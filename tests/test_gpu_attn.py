@@ -9,7 +9,7 @@ import torch
 
 import workloads as wl
 import sparse_mla_attention_fp8_amd as smla
-from tests.gpu_util import (DEV, assert_parity, build_cache, oracle_for, run_attn, to_f64)
+from tests.gpu_util import (DEV, assert_parity, bf16_dev, build_cache, oracle_for, run_attn, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -488,3 +488,76 @@ def test_four_wave_cache_beyond_4_gib(rope_dim):
     ref_out, ref_lse = oracle_attn.sparse_mla_attn(q, host, idx, W, rope_dim, sm)
     del cache
     assert_parity(out, lse, ref_out, ref_lse, range(T))
+
+
+# ---- two or three splits per row (eight-wavefront workgroups): the split of a
+# row that finishes last merges the row inside the main launch
+
+def _splits(T, H):
+    return min(256 // (T * ((H + 15) // 16)), 34)
+
+
+@pytest.mark.parametrize("kind,T,H", [("nope", 100, 16), ("rope", 90, 16), ("nope", 40, 32),
+                                        ("rope", 70, 16), ("nope", 85, 3)])
+def test_fused_merge_every_row(kind, T, H):
+    print(f"fused merge {kind} T={T} H={H}", flush=True)
+    assert 2 <= _splits(T, H) <= 3
+    if kind == "nope":
+        cfg = wl.config_nope_decode(T, seed=840 + T, num_slots=16384, ctx=(512, 16000), H=H)
+    else:
+        cfg = wl.config_rope_decode(T, seed=840 + T, num_slots=32768, ctx=(2048, 32000), H=H)
+    cache = build_cache(cfg)
+    out, lse = run_attn(cfg, cache)
+    rows = range(T)
+    ref_out, ref_lse = oracle_for(cfg, rows)
+    assert_parity(out, lse, ref_out, ref_lse, rows)
+
+
+def test_fused_merge_empty_and_short_rows():
+    """100 rows (two splits each) of 0, 1, 2, 63..65, 127..129 and random
+    entry counts with padding spread through the buffer: a split with no entry
+    adds nothing to the merge, and a row with none gives zeros and -inf."""
+    cfg = wl.config_nope_decode(100, seed=850, num_slots=16384, ctx=(600, 12000))
+    rng = np.random.default_rng(13)
+    W = cfg["W"]
+    idx = np.full((100, W), -1, dtype=np.int32)
+    counts = [0, 1, 2, 63, 64, 65, 127, 128, 129, 2048]
+    for t in range(100):
+        n = counts[t % len(counts)] if t < 40 else int(rng.integers(0, W + 1))
+        pos = rng.choice(W, size=n, replace=False)
+        idx[t, pos] = rng.choice(np.arange(1, 16384), size=n, replace=False)
+    cache = build_cache(cfg)
+    out, lse = run_attn(cfg, cache, idx=idx)
+    empty = np.nonzero((idx < 0).all(axis=1))[0]
+    assert empty.size > 0
+    assert torch.all(out[torch.from_numpy(empty).to(DEV)] == 0)
+    assert torch.all(torch.isneginf(lse[torch.from_numpy(empty).to(DEV)]))
+    rows = range(100)
+    ref_out, ref_lse = oracle_for(cfg, rows, idx=idx)
+    assert_parity(out, lse, ref_out, ref_lse, rows)
+
+
+def test_fused_merge_workspace_contents_do_not_matter():
+    """The arrival words may start in any state: workspaces of random bytes,
+    of 0xFF and of zeros, each shared by calls of other sizes in turn (a
+    16-split call's partials land where the fused calls' words were), give the
+    bits of a call on a fresh workspace every time."""
+    cfg = wl.config_nope_decode(100, seed=860, num_slots=16384, ctx=(512, 16000))
+    cache = build_cache(cfg)
+    q = bf16_dev(cfg["q"])
+    idx = torch.from_numpy(cfg["idx"]).to(DEV)
+    sizes = (100, 70, 16, 85)
+    assert [_splits(T, 16) for T in sizes] == [2, 3, 16, 3]
+    ref = {T: smla.attn(q[:T].contiguous(), cache, idx[:T], cfg["sm_scale"], 0) for T in sizes}
+    need = max(smla.workspace_size(T, 16, cfg["W"], 0) for T in sizes)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(14)
+    for fill in ("random", "ff", "zero"):
+        if fill == "random":
+            ws = torch.randint(0, 256, (need,), dtype=torch.uint8, device=DEV, generator=gen)
+        else:
+            ws = torch.full((need,), 0xFF if fill == "ff" else 0, dtype=torch.uint8, device=DEV)
+        for T in sizes + sizes:
+            o, l = smla.attn(q[:T].contiguous(), cache, idx[:T], cfg["sm_scale"], 0, workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(o, ref[T][0]) and torch.equal(l, ref[T][1]), (fill, T)

@@ -31,10 +31,12 @@ def _new_slots(idx: np.ndarray) -> np.ndarray:
     return np.array(out, dtype=np.int64)
 
 
-@pytest.mark.parametrize("T", [1, 16, 256])
+@pytest.mark.parametrize("T", [1, 16, 100, 256])
 def test_decode_step_graph_replays(T):
-    """T = 1 and 16 run the split plan and its merge kernel; T = 256 one split
-    per row."""
+    """T = 1 and 16 run the split plan and its merge kernel, T = 100 two splits
+    merged inside the launch (whose arrival words each replay must leave
+    clean, also with eager calls on the same workspace between replays), and
+    T = 256 one split per row."""
     print(f"graph decode step T={T}", flush=True)
     cfg = wl.config_nope_decode(T, seed=900 + T, num_slots=16384, ctx=(512, 16000))
     cache = build_cache(cfg)
@@ -74,7 +76,7 @@ def test_decode_step_graph_replays(T):
         # eager work on the same buffers: other rows into the same slots, and
         # an attention call over them into fresh outputs
         smla.kv_write(lat_other, None, slots, cache)
-        o2, _ = smla.attn(q, cache, idx, cfg["sm_scale"], 0, topk_capacity=W)
+        o2, _ = smla.attn(q, cache, idx, cfg["sm_scale"], 0, topk_capacity=W, workspace=ws)
         out.zero_()
         lse.fill_(float("nan"))
         torch.cuda.synchronize()

@@ -26,7 +26,7 @@ def _both(cfg, cache, T):
     return out, lse, ref_out, ref_lse
 
 
-@pytest.mark.parametrize("kind,T1,T2", [("nope", 16, 4), ("rope", 64, 1), ("nope", 1, 256)])
+@pytest.mark.parametrize("kind,T1,T2", [("nope", 16, 4), ("rope", 64, 1), ("nope", 1, 256), ("nope", 100, 70)])
 def test_noalloc_matches_workspace_entry_point(kind, T1, T2):
     print(f"noalloc {kind} T={T1} then T={T2}", flush=True)
     if kind == "nope":
