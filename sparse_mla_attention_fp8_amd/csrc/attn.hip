@@ -59,6 +59,7 @@
 #include "common.h"
 
 #include <atomic>
+#include <chrono>
 #include <random>
 
 namespace smla {
@@ -1565,8 +1566,14 @@ hipError_t launch_merge(const float* part_o, const float* part_ml, int splits, i
 // 2^56), from a random start so that no leftover workspace word matches one.
 unsigned long long next_epoch() {
   static std::atomic<unsigned long long> counter{[] {
-    std::random_device rd;
-    return ((((unsigned long long)rd() << 32) | rd()) >> 9) | 1ull;
+    unsigned long long seed = (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count();
+    try {
+      std::random_device rd;
+      seed ^= ((unsigned long long)rd() << 32) | rd();
+    } catch (...) {
+      // no entropy source: the clock alone still differs between processes
+    }
+    return seed;
   }()};
   return counter.fetch_add(1, std::memory_order_relaxed) % ((1ull << 56) - 1) + 1;
 }
