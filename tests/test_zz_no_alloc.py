@@ -74,14 +74,15 @@ def test_noalloc_refuses_plans_beyond_the_scratch():
     assert bool((out == 7.0).all())               # nothing was launched
 
 
-def test_noalloc_in_a_graph():
-    """The call captured in a HIP graph (split plan and merge, T = 16): every
-    replay, with eager calls that use the same scratch between replays, gives
-    the workspace entry point's bytes."""
-    print("noalloc graph T=16", flush=True)
-    cfg = wl.config_nope_decode(16, seed=313, num_slots=16384, ctx=(512, 16384))
+@pytest.mark.parametrize("T", [16, 100])
+def test_noalloc_in_a_graph(T):
+    """The call captured in a HIP graph (T = 16: sixteen splits and the merge
+    kernel; T = 100: two splits merged inside the launch, whose arrival words
+    live in the scratch too): every replay, with eager calls that use the same
+    scratch between replays, gives the workspace entry point's bytes."""
+    print(f"noalloc graph T={T}", flush=True)
+    cfg = wl.config_nope_decode(T, seed=313, num_slots=16384, ctx=(512, 16000))
     cache = build_cache(cfg)
-    T = 16
     q = bf16_dev(cfg["q"])
     idx = torch.from_numpy(cfg["idx"]).to(DEV)
     ref_out, ref_lse = smla.attn(q, cache, idx, cfg["sm_scale"], 0)
