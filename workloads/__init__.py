@@ -251,3 +251,47 @@ def config_writer(N: int = 8192, rope_dim: int = ROPE, seed: int = 50,
     cache[0] = 0
     return dict(num_slots=num_slots, rope_dim=rope_dim, N=N, latent=latent,
                 rope=rope, slots=slots, cache=cache)
+
+
+def config_random_shape(seed: int) -> dict:
+    """A call of random shape for sweep tests: rope 0 or 64, T, H and the
+    buffer width W drawn across the launch plan's boundaries (one or many
+    splits, two or three merged in the launch, four-wavefront workgroups,
+    buffers wider than one scan), a small cache, and top-k rows whose valid
+    count, padding positions, duplicates and out-of-range entries vary per row.
+    `idx` may be wider than W (its extra columns are junk the call must not
+    read); `stride_extra` says by how much.  Slot 0 is listed only when its
+    bytes are zeros."""
+    rng = np.random.default_rng(900_000 + seed)
+    rope_dim = int(rng.choice([0, ROPE]))
+    T = int(rng.choice([1, 2, 3, 7, 16, 33, 64, 65, 100, 128, 129, 200, 256, 257, 300, 513]))
+    H = int(rng.choice([1, 3, 8, 16, 17, 32, 48]))
+    W = int(rng.choice([1, 7, 64, 65, 300, 2048, 2176, 2304, 2305, 3000]))
+    num_slots = int(rng.choice([1024, 2048, 4096]))
+    stride_extra = int(rng.choice([0, 0, 5]))
+    poison = str(rng.choice(["ff", "7f", "random", "zero"]))
+    # slot 0 is listed only when it holds zeros: it is read like any other
+    # slot, and NaN-coded bytes there would make the listing rows NaN
+    lo = 0 if poison == "zero" else 1
+    latent, rope, slots = cache_rows(rng, num_slots, rope_dim)
+    q = normal_bf16(rng, (T, H, LATENT + rope_dim))
+    idx = np.full((T, W + stride_extra), -1, dtype=np.int32)
+    if stride_extra:
+        idx[:, W:] = rng.integers(0, num_slots, size=(T, stride_extra), dtype=np.int32)
+    for t in range(T):
+        kind = rng.integers(0, 8)
+        if kind == 0:
+            n = 0                                  # an empty row
+        elif kind == 1:
+            n = W                                  # a full row
+        else:
+            n = int(rng.integers(0, W + 1))
+        pos = rng.choice(W, size=n, replace=False)
+        vals = rng.integers(lo, num_slots, size=n, dtype=np.int64)   # repeats included
+        if n and rng.integers(0, 4) == 0:          # some out-of-range padding
+            bad = rng.random(n) < 0.1
+            vals[bad] = rng.choice([-7, num_slots, num_slots + 1000, 2**31 - 1], size=int(bad.sum()))
+        idx[t, pos] = vals.astype(np.int32)
+    return dict(num_slots=num_slots, rope_dim=rope_dim, T=T, H=H, W=W, stride_extra=stride_extra,
+                latent=latent, rope=rope, slots=slots, q=q, idx=idx,
+                sm_scale=float(1.0 / np.sqrt(LATENT + rope_dim)), slot0=slot0_bytes(rng, poison))
