@@ -1,5 +1,6 @@
 """HIP writer vs the oracle writer: byte-exact rows, dropped padding rows,
-untouched bytes, NoPE zero tail, and a sweep of every bf16 value."""
+untouched bytes, NoPE zero tail, a sweep of every bf16 value and of every
+reachable scale, and calls of random shape."""
 import numpy as np
 import pytest
 import torch
@@ -185,3 +186,43 @@ def test_nan_input_in_a_kept_row():
         keep[512 + 4 * tile:516 + 4 * tile] = False
         assert np.array_equal(got[row][keep], want[row][keep])
     assert np.array_equal(got[[0, 1, 4]], want[[0, 1, 4]])
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_writer_random_calls(seed):
+    """Writer calls of random shape, byte for byte against the oracle over the
+    whole cache: ragged row counts, rope 0 or 64, inputs as column views of a
+    wider tensor, rows scaled across binades with zero tiles, and padding rows
+    (slot 0, negative, past the cache) holding NaN inputs; every byte the call
+    must not write keeps its 0xA5 fill."""
+    rng = np.random.default_rng(700 + seed)
+    rope_dim = int(rng.choice([0, 64]))
+    n = int(rng.choice([1, 2, 3, 4, 5, 63, 64, 65, 255, 256, 257, 1000, 4097]))
+    num_slots = int(rng.choice([300, 4096, 70000]))
+    pad_cols = int(rng.choice([0, 64, 576]))
+    print(f"writer sweep seed={seed} n={n} rope={rope_dim} slots={num_slots} pad={pad_cols}", flush=True)
+    width = 512 + rope_dim + pad_cols
+    x = wl.f32_from_bf16_bits(wl.normal_bf16(rng, (n, width)))
+    x *= np.exp2(rng.integers(-60, 60, size=(n, 1))).astype(np.float32)
+    zero_tile = rng.random((n, 4)) < 0.05
+    for t in range(4):
+        x[zero_tile[:, t], 128 * t:128 * (t + 1)] = 0.0
+    full = wl.bf16_bits_from_f32(x.astype(np.float32))
+    keep = min(n, num_slots - 1)
+    slots = np.empty(n, dtype=np.int64)
+    slots[:keep] = rng.choice(np.arange(1, num_slots), size=keep, replace=False)
+    slots[keep:] = 0
+    pad = rng.random(n) < 0.2
+    slots[pad] = rng.choice([0, -1, -9, num_slots, num_slots + 77], size=int(pad.sum()))
+    full[slots <= 0] = wl.BF16_QNAN
+    full[slots >= num_slots] = wl.BF16_QNAN
+    t_full = bf16_dev(full)
+    lat_t = t_full[:, :512]
+    rope_t = t_full[:, 512:512 + rope_dim] if rope_dim else None
+    cache0 = np.full((num_slots, 656), 0xA5, dtype=np.uint8)
+    cfg = dict(cache=cache0, latent=full[:, :512], rope=full[:, 512:512 + rope_dim] if rope_dim else None,
+               slots=slots)
+    got = _run(cfg, lat=lat_t, rope=rope_t)
+    want = cache0.copy()
+    oracle_writer.kv_write(want, full[:, :512], full[:, 512:512 + rope_dim] if rope_dim else None, slots)
+    assert np.array_equal(got, want)
