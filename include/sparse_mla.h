@@ -275,7 +275,9 @@ int mla_gather_upconvert(const void* kv_cache, int64_t num_slots, int rope_dim,
  * pages           int32 [num_pages], the touched source pages.
  * dst             uint8, >= 4 * num_src_pages pages of dst_page_stride bytes
  *                 (>= 64 * row_bytes, a multiple of 16), 16-byte aligned.
- * row_bytes       bytes per token row (656 for fp8_ds_mla), a multiple of 16.
+ * row_bytes       bytes per token row, >= 1 (656 for fp8_ds_mla; any size,
+ *                 e.g. 585 for the 37,440-byte 64-token page, since 64 rows
+ *                 always span a multiple of 16 bytes).
  */
 int mla_split_pages_64(const void* src_pool, int64_t num_src_pages, int64_t src_page_stride,
                        const int32_t* pages, int64_t num_pages,

@@ -263,8 +263,8 @@ int mla_split_pages_64(const void* src_pool, int64_t num_src_pages, int64_t src_
                        const int32_t* pages, int64_t num_pages, void* dst, int64_t dst_page_stride,
                        int row_bytes, hipStream_t stream) {
   g_err[0] = '\0';
-  if (row_bytes < 16 || (row_bytes & 15))
-    return fail(SMLA_EINVAL, "mla_split_pages_64: row_bytes must be a positive multiple of 16, got %d", row_bytes);
+  if (row_bytes < 1)
+    return fail(SMLA_EINVAL, "mla_split_pages_64: row_bytes must be positive, got %d", row_bytes);
   if (num_src_pages < 1 || num_pages < 0)
     return fail(SMLA_EINVAL, "mla_split_pages_64: need num_src_pages >= 1 and num_pages >= 0");
   if (num_pages == 0) return SMLA_OK;

@@ -32,7 +32,9 @@ __global__ __launch_bounds__(kSplitThreads) void split_pages_kernel(
   const int32_t p = pages[item >> 2];
   if (p < 0 || p >= num_src_pages) return;
   const int k = (int)(item & 3);
-  const int64_t bytes = 64 * (int64_t)row_bytes;   // a multiple of 1,024
+  // 64 rows: a multiple of 64 bytes whatever the row size (585-byte rows
+  // make the 37,440-byte page), so every quarter is 16-byte aligned
+  const int64_t bytes = 64 * (int64_t)row_bytes;
   const uint4* s = reinterpret_cast<const uint4*>(src + p * src_page_stride + k * bytes);
   uint4* d = reinterpret_cast<uint4*>(dst + (4 * (int64_t)p + k) * dst_page_stride);
   const int64_t n16 = bytes / 16;

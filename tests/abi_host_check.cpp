@@ -185,6 +185,8 @@ int main() {
   expect("pages row bytes", mla_split_pages_64(P, 8, INT64_MAX, idx, 4, Q, 64 * 656, INT_MAX - 15, s),
          SMLA_EINVAL);
   expect("pages stride", mla_split_pages_64(P, 8, INT64_MIN, idx, 4, Q, 64 * 656, 656, s), SMLA_EINVAL);
+  expect("pages 585-byte rows", mla_split_pages_64(P, 8, 256 * 585, idx, 4, Q, 64 * 585, 585, s), SMLA_OK);
+  expect("pages 0-byte rows", mla_split_pages_64(P, 8, 256 * 656, idx, 4, Q, 64 * 656, 0, s), SMLA_EINVAL);
 
   auto* sink = reinterpret_cast<uint32_t*>(buf + 1024);
   expect("probe ok", smla_gather_rows_probe(P, 4096, 0, idx, 1000, sink, s), SMLA_OK);

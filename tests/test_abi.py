@@ -147,7 +147,7 @@ def test_split_pages_validation():
     base = dict(src=FAKE, num_src=8, src_stride=256 * 656, pages=FAKE, num_pages=4,
                 dst=FAKE + 0x1000000, dst_stride=64 * 656, row_bytes=656, stream=None)
     bad = [
-        dict(row_bytes=0), dict(row_bytes=650), dict(num_src=0), dict(num_pages=-1),
+        dict(row_bytes=0), dict(row_bytes=-16), dict(num_src=0), dict(num_pages=-1),
         dict(src=None), dict(pages=None), dict(dst=None),
         dict(src_stride=256 * 656 - 16), dict(dst_stride=64 * 656 - 16), dict(dst_stride=64 * 656 + 8),
         dict(src=FAKE + 8), dict(pages=FAKE + 2),

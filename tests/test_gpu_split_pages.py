@@ -14,7 +14,7 @@ from tests.gpu_util import DEV, bf16_dev, build_cache, to_f64
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("row_bytes,pad,with_page0", [(656, 0, False), (656, 48, True), (1024, 16, False)])
+@pytest.mark.parametrize("row_bytes,pad,with_page0", [(656, 0, False), (656, 48, True), (1024, 16, False), (585, 0, True)])
 def test_split_byte_exact(row_bytes, pad, with_page0):
     print(f"split rb={row_bytes} pad={pad} page0={with_page0}", flush=True)
     rng = np.random.default_rng(row_bytes + pad)
