@@ -994,9 +994,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void attn_mfma_kern
       part_ml[2 * pidx + 1] = L;
     }
   } else if constexpr (WAVES == 8) {
-    // The row's partials, [split][head][512] and [split][head](m, l) from its
-    // first head, reached through device-coherent accesses: every split stores
-    // its own, and the split that arrives last reads them all back.
+    // The row's partials, O [split][head][512] and (m, l) [split][head], through
+    // buffer resources based at the row's first entries and device-coherent
+    // accesses: every split stores its own, and the split that arrives last
+    // reads the others back.
     const int64_t row0 = (int64_t)t * splits * H;
     const uint32_t o_bytes = (uint32_t)(splits * H * kLatent * 4);
     const __amdgpu_buffer_rsrc_t ro = coherent_rsrc(part_o + row0 * kLatent, o_bytes);

@@ -9,7 +9,7 @@ import torch
 
 import workloads as wl
 import sparse_mla_attention_fp8_amd as smla
-from tests.gpu_util import (DEV, assert_parity, bf16_dev, build_cache, oracle_for, run_attn, to_f64)
+from tests.gpu_util import DEV, assert_parity, bf16_dev, build_cache, oracle_for, run_attn
 
 pytestmark = pytest.mark.gpu
 

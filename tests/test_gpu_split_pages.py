@@ -9,7 +9,7 @@ import torch
 import workloads as wl
 import sparse_mla_attention_fp8_amd as smla
 from oracle import pages as oracle_pages
-from tests.gpu_util import DEV, bf16_dev, build_cache, to_f64
+from tests.gpu_util import DEV, bf16_dev, build_cache
 
 pytestmark = pytest.mark.gpu
 
