@@ -180,7 +180,9 @@ int sparse_mla_attn(const void* q,
  * size with topk_capacity <= 2304 fits: it needs at most 8.03 MiB).
  * All calls on one GPU share its scratch: calls that overlap on one GPU (on
  * different streams, or from different threads) race and must not be issued.
- * Nothing in the scratch needs to start at zero.
+ * Nothing in the scratch needs to start at zero (with two or three splits per
+ * row it also holds the words that find the split finishing last, which each
+ * call leaves zero).
  */
 #define SMLA_NOALLOC_SCRATCH_BYTES (16u << 20)
 int sparse_mla_attn_noalloc(const void* q,
