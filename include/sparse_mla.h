@@ -61,6 +61,11 @@
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
+/* The library exports its entry points and nothing else. */
+#ifndef SMLA_API
+#define SMLA_API __attribute__((visibility("default")))
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -102,7 +107,7 @@ extern "C" {
  * num_rows        >= 0 (0 launches nothing).
  * kv_cache        uint8 [num_slots][656], 16-byte aligned; num_slots >= 1.
  */
-int mla_kv_write(const void* kv_c, int64_t kv_c_row_stride,
+SMLA_API int mla_kv_write(const void* kv_c, int64_t kv_c_row_stride,
                  const void* k_pe, int64_t k_pe_row_stride,
                  int rope_dim,
                  const int64_t* slot_mapping, int64_t num_rows,
@@ -114,7 +119,7 @@ int mla_kv_write(const void* kv_c, int64_t kv_c_row_stride,
  * sparse_mla_attn needs for these sizes (0 when none is needed).  Pure host
  * function; returns 0 for invalid sizes as well (sparse_mla_attn reports them).
  */
-size_t sparse_mla_attn_workspace_size(int T, int H, int topk_capacity, int rope_dim);
+SMLA_API size_t sparse_mla_attn_workspace_size(int T, int H, int topk_capacity, int rope_dim);
 
 /*
  * sparse_mla_attn - sparse MLA attention over the fp8_ds_mla cache.
@@ -154,7 +159,7 @@ size_t sparse_mla_attn_workspace_size(int T, int H, int topk_capacity, int rope_
  *                 words that find the split finishing last, which each call
  *                 leaves zero); two calls that share it must not overlap.
  */
-int sparse_mla_attn(const void* q,
+SMLA_API int sparse_mla_attn(const void* q,
                     const void* kv_cache, int64_t num_slots,
                     const int32_t* topk_idx, int64_t idx_row_stride, int topk_capacity,
                     int T, int H, int rope_dim, float sm_scale,
@@ -185,7 +190,7 @@ int sparse_mla_attn(const void* q,
  * call leaves zero).
  */
 #define SMLA_NOALLOC_SCRATCH_BYTES (16u << 20)
-int sparse_mla_attn_noalloc(const void* q,
+SMLA_API int sparse_mla_attn_noalloc(const void* q,
                             const void* kv_cache, int64_t num_slots,
                             const int32_t* topk_idx, int64_t idx_row_stride, int topk_capacity,
                             int T, int H, int rope_dim, float sm_scale,
@@ -203,7 +208,7 @@ int sparse_mla_attn_noalloc(const void* q,
  * dropped and their inputs never read.  Arguments as for mla_kv_write, except
  * kv_cache: bf16 [num_slots][512 + rope_dim], 16-byte aligned.
  */
-int mla_kv_write_bf16(const void* kv_c, int64_t kv_c_row_stride,
+SMLA_API int mla_kv_write_bf16(const void* kv_c, int64_t kv_c_row_stride,
                       const void* k_pe, int64_t k_pe_row_stride,
                       int rope_dim,
                       const int64_t* slot_mapping, int64_t num_rows,
@@ -221,7 +226,7 @@ int mla_kv_write_bf16(const void* kv_c, int64_t kv_c_row_stride,
  * the workspace (same size as sparse_mla_attn_workspace_size) and the error
  * behaviour are those of sparse_mla_attn.
  */
-int sparse_mla_attn_bf16(const void* q,
+SMLA_API int sparse_mla_attn_bf16(const void* q,
                          const void* kv_cache, int64_t num_slots,
                          const int32_t* topk_idx, int64_t idx_row_stride, int topk_capacity,
                          int T, int H, int rope_dim, float sm_scale,
@@ -252,7 +257,7 @@ int sparse_mla_attn_bf16(const void* q,
  *                 576 .. dst_row_stride-1 are not written.
  * dst_row_stride  elements, >= 576 and a multiple of 8.
  */
-int mla_gather_upconvert(const void* kv_cache, int64_t num_slots, int rope_dim,
+SMLA_API int mla_gather_upconvert(const void* kv_cache, int64_t num_slots, int rope_dim,
                          const int64_t* slots, int64_t num_rows,
                          void* dst, int64_t dst_row_stride, hipStream_t stream);
 
@@ -281,7 +286,7 @@ int mla_gather_upconvert(const void* kv_cache, int64_t num_slots, int rope_dim,
  *                 e.g. 585 for the 37,440-byte 64-token page, since 64 rows
  *                 always span a multiple of 16 bytes).
  */
-int mla_split_pages_64(const void* src_pool, int64_t num_src_pages, int64_t src_page_stride,
+SMLA_API int mla_split_pages_64(const void* src_pool, int64_t num_src_pages, int64_t src_page_stride,
                        const int32_t* pages, int64_t num_pages,
                        void* dst, int64_t dst_page_stride, int row_bytes,
                        hipStream_t stream);
@@ -308,11 +313,11 @@ int mla_split_pages_64(const void* src_pool, int64_t num_src_pages, int64_t src_
  * out             bf16 [T][H][512], 16-byte aligned; must not overlap the parts.
  * lse             float32 [T][H], or NULL.
  */
-int sparse_mla_merge(const void* part_out, const float* part_lse, int P, int T, int H,
+SMLA_API int sparse_mla_merge(const void* part_out, const float* part_lse, int P, int T, int H,
                      void* out, float* lse, hipStream_t stream);
 
 /* Thread-local description of the last error returned on this thread ("" if none). */
-const char* smla_last_error(void);
+SMLA_API const char* smla_last_error(void);
 
 #ifdef __cplusplus
 }

@@ -11,6 +11,11 @@
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
+/* The library exports its entry points and nothing else. */
+#ifndef SMLA_API
+#define SMLA_API __attribute__((visibility("default")))
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -36,7 +41,7 @@ extern "C" {
  * Errors as for the other calls: SMLA_EINVAL for bad arguments, SMLA_EUNSUPPORTED
  * for n beyond the limit, SMLA_ELAUNCH if the launch fails.
  */
-int smla_gather_rows_probe(const void* kv_cache, int64_t num_slots, int rope_dim,
+SMLA_API int smla_gather_rows_probe(const void* kv_cache, int64_t num_slots, int rope_dim,
                            const int32_t* slots, int64_t n, uint32_t* sink, hipStream_t stream);
 
 #ifdef __cplusplus

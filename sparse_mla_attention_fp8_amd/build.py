@@ -21,12 +21,13 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CXX = os.environ.get("CXX", "g++")
 ARCH = "gfx950"
 FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",
+    f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall", "-fvisibility=hidden",
     # keep the compiler from forming packed-fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fno-gpu-rdc",
 ]
-HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include"]
+HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall", "-fvisibility=hidden", "-D__HIP_PLATFORM_AMD__",
+              "-I/opt/rocm/include"]
 
 
 def build(verbose: bool = False) -> str:

@@ -19,7 +19,7 @@ def _declared():
     for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
         text = open(h).read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-        for m in re.finditer(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M):
+        for m in re.finditer(r"^\s*(?:SMLA_API\s+)?(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M):
             names.add(m.group(1))
     return names
 
@@ -32,6 +32,16 @@ def test_every_declared_symbol_is_exported():
     for n in names:
         assert hasattr(raw, n), n
     assert set(smla._SIGS) == names
+
+
+def test_only_the_declared_entry_points_are_exported():
+    """The library's internal C++ symbols stay hidden (built with hidden
+    visibility; the headers mark the entry points for export)."""
+    names = _declared()
+    out = subprocess.run(["nm", "-D", "--defined-only", smla.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    functions = {line.split()[-1] for line in out.splitlines() if len(line.split()) == 3 and line.split()[1] == "T"}
+    assert functions == names, sorted(functions ^ names)
 
 
 FAKE = 0x10000          # an aligned address that is never dereferenced
