@@ -45,3 +45,26 @@ def test_disjoint_and_writer_configs():
     w = wl.config_writer(N=1024, num_slots=4096)
     assert (w["slots"] == 0).sum() == 256 and np.all(w["latent"][768:] == wl.BF16_QNAN)
     assert len(set(w["slots"][:768].tolist())) == 768 and w["slots"][:768].min() >= 1
+
+
+def test_random_shape_configs():
+    """The sweep generator: deterministic per seed, shapes inside the drawn
+    lists, idx at least W wide with junk only past W, slot 0 listed only when
+    its bytes are zeros, and every valid entry below num_slots."""
+    seen = set()
+    for seed in range(64):
+        a, b = wl.config_random_shape(seed), wl.config_random_shape(seed)
+        assert np.array_equal(a["idx"], b["idx"]) and np.array_equal(a["q"], b["q"])
+        T, H, W = a["T"], a["H"], a["W"]
+        assert a["idx"].shape == (T, W + a["stride_extra"])
+        assert a["q"].shape == (T, H, wl.LATENT + a["rope_dim"])
+        assert a["latent"].shape == (a["num_slots"] - 1, wl.LATENT)
+        active = a["idx"][:, :W]
+        valid = (active >= 0) & (active < a["num_slots"])
+        if (active == 0).any():
+            assert not a["slot0"].any()
+        seen.add((T * ((H + 15) // 16) > 256, W > 2304, bool((~valid.any(axis=1)).any())))
+    # the draws reach both workgroup shapes, wide buffers and empty rows
+    assert {s[0] for s in seen} == {False, True}
+    assert {s[1] for s in seen} == {False, True}
+    assert True in {s[2] for s in seen}
