@@ -1027,9 +1027,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void attn_mfma_kern
     if (*last == 0) return;
     // The last split merges the row where its own values already are: each
     // writer lane combines its 32 outputs (head n16, dims dim0 + 16cc + r)
-    // over the splits in split order, its own from registers and the others'
-    // read back, with the merge kernels' arithmetic (M = max m_s, weights
-    // 2^(m_s - M), O = sum w_s O_s / sum w_s l_s).
+    // over the splits in split order, its own O from registers and the others'
+    // read back, with the merge kernels' inputs and arithmetic (M = max m_s,
+    // weights 2^(m_s - M), O = sum w_s O_s / sum w_s l_s), so the bits do not
+    // depend on which split is last.
     if (ps == 1 || !hvalid) return;
     float ms[kFusedMaxSplits], ls[kFusedMaxSplits];
     f4 a[kFusedMaxSplits][8];
@@ -1037,9 +1038,14 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void attn_mfma_kern
     for (int j = 0; j < kFusedMaxSplits; ++j) {
       const bool load = j < splits && j != split;
       const uint32_t hm = (uint32_t)(j * H + head);
-      const v2i mlv = load ? __builtin_amdgcn_raw_buffer_load_b64(rm, hm * 8, 0, kDeviceScope) : v2i{0, 0};
-      ms[j] = j == split ? M : (load ? __uint_as_float((uint32_t)mlv[0]) : -INFINITY);
-      ls[j] = j == split ? L : (load ? __uint_as_float((uint32_t)mlv[1]) : 0.0f);
+      // Every split's (m, l), this one's included, is read back: a lane's own
+      // l can differ in its last bits from the stored one (the P.V wavefronts
+      // of the four dim tiles round their exponentials with different
+      // normalisers), and using it would make the bits depend on which split
+      // happens to finish last.
+      const v2i mlv = j < splits ? __builtin_amdgcn_raw_buffer_load_b64(rm, hm * 8, 0, kDeviceScope) : v2i{0, 0};
+      ms[j] = j < splits ? __uint_as_float((uint32_t)mlv[0]) : -INFINITY;
+      ls[j] = j < splits ? __uint_as_float((uint32_t)mlv[1]) : 0.0f;
 #pragma unroll
       for (int cc = 0; cc < 8; ++cc)
         a[j][cc] = load ? __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(

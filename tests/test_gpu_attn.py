@@ -537,6 +537,36 @@ def test_fused_merge_empty_and_short_rows():
     assert_parity(out, lse, ref_out, ref_lse, rows)
 
 
+def test_fused_merge_bits_do_not_depend_on_the_last_split():
+    """Which split of a row arrives last varies from call to call (here also
+    through the arrival words' starting contents, which add a retry to some
+    arrivals); the merged bits must not.  These 100 rows (two splits each)
+    hold an output within a rounding step of a bf16 tie (row 25, head 1, dim
+    371), so a merge that weighs the last split by its own lane's copy of l,
+    which can differ in its last bits from the stored one, flips it."""
+    cfg = wl.config_nope_decode(300, seed=870, num_slots=16384, ctx=(512, 16000))
+    cache = build_cache(cfg)
+    T = 100
+    assert _splits(T, 16) == 2
+    q = bf16_dev(cfg["q"][:T])
+    idx = torch.from_numpy(np.ascontiguousarray(cfg["idx"][:T])).to(DEV)
+    need = smla.workspace_size(T, 16, cfg["W"], 0)
+    ref = None
+    for i in range(24):
+        if i % 3 == 0:
+            ws = torch.full((need,), 0xA5, dtype=torch.uint8, device=DEV)
+        elif i % 3 == 1:
+            ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+        else:
+            ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+        o, l = smla.attn(q, cache, idx, cfg["sm_scale"], 0, workspace=ws)
+        torch.cuda.synchronize()
+        if ref is None:
+            ref = (o, l)
+        else:
+            assert torch.equal(o, ref[0]) and torch.equal(l, ref[1]), i
+
+
 def test_fused_merge_workspace_contents_do_not_matter():
     """The arrival words may start in any state: workspaces of random bytes,
     of 0xFF and of zeros, each shared by calls of other sizes in turn (a
