@@ -102,3 +102,63 @@ def test_write_then_attend_on_two_streams():
         assert torch.equal(caches[k], ref[k][0]), k
         for r in range(REPS):
             assert torch.equal(outs[k][r], ref[k][1][0]) and torch.equal(lses[k][r], ref[k][1][1]), (k, r)
+
+
+def test_results_do_not_depend_on_memory_load():
+    """Every plan kind, the BF16 path, the gather and the writer give the same
+    bits while another stream keeps HBM busy with large copies: latencies
+    change, so a wait that were too short for its loads, or any other
+    dependence on timing, would show."""
+    print("calls under a background copy load", flush=True)
+    cfg = wl.config_nope_decode(300, seed=890, num_slots=16384, ctx=(512, 16000))
+    cache = build_cache(cfg)
+    pf = wl.config_prefill(1024, seed=891, num_slots=8192)
+    pcache = build_cache(pf)
+    bcache = torch.zeros((cfg["num_slots"], 512), dtype=torch.bfloat16, device=DEV)
+    smla.kv_write_bf16(bf16_dev(cfg["latent"]), None, torch.from_numpy(cfg["slots"]).to(DEV), bcache)
+    q = bf16_dev(cfg["q"])
+    idx = torch.from_numpy(cfg["idx"]).to(DEV)
+    pq = bf16_dev(pf["q"])
+    pidx = torch.from_numpy(pf["idx"]).to(DEV)
+    rng = np.random.default_rng(892)
+    gslots = torch.from_numpy(rng.integers(0, cfg["num_slots"], size=4096).astype(np.int64)).to(DEV)
+    wlat = bf16_dev(wl.normal_bf16(rng, (512, 512)))
+    wslots = torch.from_numpy(rng.choice(np.arange(1, cfg["num_slots"]), 512, replace=False).astype(np.int64)).to(DEV)
+    torch.cuda.synchronize()
+
+    def fp8(T):
+        return lambda: smla.attn(q[:T].contiguous(), cache, idx[:T], cfg["sm_scale"], 0)
+
+    def bf(T):
+        return lambda: smla.attn_bf16(q[:T].contiguous(), bcache, idx[:T], cfg["sm_scale"])
+
+    def write():
+        c = cache.clone()
+        smla.kv_write(wlat, None, wslots, c)
+        return (c,)
+
+    calls = [("fp8 T=%d" % T, fp8(T)) for T in (1, 16, 64, 100, 256, 300)]
+    calls += [("bf16 T=%d" % T, bf(T)) for T in (16, 256)]
+    calls += [("prefill 1024", lambda: smla.attn(pq, pcache, pidx, pf["sm_scale"], 64)),
+              ("gather", lambda: (smla.gather_upconvert(cache, gslots, 0),)),
+              ("writer", write)]
+    quiet = {}
+    for name, f in calls:
+        quiet[name] = [t.clone() for t in f() if t is not None]
+        torch.cuda.synchronize()
+
+    src = torch.empty(256 << 20, dtype=torch.uint8, device=DEV)
+    dst = torch.empty_like(src)
+    bg = torch.cuda.Stream()
+    bg.wait_stream(torch.cuda.current_stream())
+    for rep in range(3):
+        got = {}
+        for name, f in calls:
+            with torch.cuda.stream(bg):
+                for _ in range(3):
+                    dst.copy_(src)
+            got[name] = f()
+        torch.cuda.synchronize()
+        for name, _ in calls:
+            res = [t for t in got[name] if t is not None]
+            assert all(torch.equal(a, b) for a, b in zip(res, quiet[name])), (rep, name)
