@@ -29,7 +29,16 @@ SEEDS = int(os.environ.get("SMLA_SWEEP_SEEDS", "96"))
 
 @pytest.mark.parametrize("seed", range(SEEDS))
 def test_random_shape(seed):
-    cfg = wl.config_random_shape(seed)
+    _check_random_call(wl.config_random_shape(seed), seed)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_shape_many_heads(seed):
+    """64 to 128 heads: several head groups per row, in every plan kind."""
+    _check_random_call(wl.config_random_shape_many_heads(seed), seed)
+
+
+def _check_random_call(cfg, seed):
     T, H, W = cfg["T"], cfg["H"], cfg["W"]
     print(f"sweep seed={seed} rope={cfg['rope_dim']} T={T} H={H} W={W} "
           f"slots={cfg['num_slots']} stride+{cfg['stride_extra']}", flush=True)

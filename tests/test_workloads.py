@@ -68,3 +68,23 @@ def test_random_shape_configs():
     assert {s[0] for s in seen} == {False, True}
     assert {s[1] for s in seen} == {False, True}
     assert True in {s[2] for s in seen}
+
+
+def test_random_shape_many_heads_configs():
+    """The many-heads draws: 64 to 128 heads, q and idx with T rows, the idx
+    rows taken from the base draw in turn, and among the first 24 seeds every
+    plan kind (four-wavefront workgroups, two or three splits merged in the
+    launch, more splits with the merge kernel)."""
+    kinds = set()
+    for seed in range(24):
+        a = wl.config_random_shape_many_heads(seed)
+        base = wl.config_random_shape(seed)
+        T, H, W = a["T"], a["H"], a["W"]
+        assert 64 <= H <= 128
+        assert a["q"].shape == (T, H, wl.LATENT + a["rope_dim"])
+        assert a["idx"].shape == (T, W + a["stride_extra"])
+        assert np.array_equal(a["idx"], base["idx"][np.arange(T) % base["T"]])
+        units = T * ((H + 15) // 16)
+        kinds.add("four-wave" if units > 256 else "one split" if units > 128 else
+                  "fused" if units > 64 else "merge kernel")
+    assert kinds >= {"four-wave", "fused", "merge kernel"}

@@ -295,3 +295,17 @@ def config_random_shape(seed: int) -> dict:
     return dict(num_slots=num_slots, rope_dim=rope_dim, T=T, H=H, W=W, stride_extra=stride_extra,
                 latent=latent, rope=rope, slots=slots, q=q, idx=idx,
                 sm_scale=float(1.0 / np.sqrt(LATENT + rope_dim)), slot0=slot0_bytes(rng, poison))
+
+
+def config_random_shape_many_heads(seed: int) -> dict:
+    """config_random_shape with 64 to 128 heads (several head groups per row)
+    and T up to 100: the same cache and list rules, rows of the drawn lists
+    reused in turn when T exceeds their count."""
+    cfg = config_random_shape(seed)
+    rng = np.random.default_rng(700_000 + seed)
+    H = int(rng.choice([64, 100, 127, 128]))
+    T = int(rng.choice([1, 2, 3, 11, 16, 21, 32, 33, 40, 64, 65, 100]))
+    cfg["q"] = normal_bf16(rng, (T, H, LATENT + cfg["rope_dim"]))
+    cfg["idx"] = np.ascontiguousarray(cfg["idx"][np.arange(T) % cfg["T"]])
+    cfg["T"], cfg["H"] = T, H
+    return cfg
