@@ -1495,13 +1495,15 @@ __global__ __launch_bounds__(64 * kMergeWaves) void attn_merge_kernel(const floa
 
 // The same combination for few splits (at most kMergeSmallMax): one wavefront
 // per (row, head), four per 256-thread block; lane l owns dims 8l..8l+7.  The
-// splits are taken eight at a time with a running maximum, every load of a
-// group issued before any is used, so up to eight splits cost one memory round
-// trip and no LDS.  The eight-wavefront kernel above wins only when there are
-// many splits to spread over its wavefronts.
+// splits are taken GROUP at a time with a running maximum, every load of a
+// group issued before any is used, so a call costs one memory round trip and
+// no LDS: groups of sixteen for nine to sixteen splits, of eight below, where
+// the wider group's registers buy nothing.  The eight-wavefront kernel above
+// wins only when there are many splits to spread over its wavefronts.
 constexpr int kMergeSmallMax = 16;
 constexpr int kMergeSmallRows = 4;
 
+template <int GROUP>
 __global__ __launch_bounds__(64 * kMergeSmallRows) void attn_merge_small_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml, int splits, int H, int rows,
     uint16_t* __restrict__ out, float* __restrict__ lse) {
@@ -1515,11 +1517,11 @@ __global__ __launch_bounds__(64 * kMergeSmallRows) void attn_merge_small_kernel(
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
   float M = -INFINITY, L = 0.0f;
-  for (int s0 = 0; s0 < splits; s0 += 8) {
-    float ms[8], ls[8];
-    float4 a[8], c[8];
+  for (int s0 = 0; s0 < splits; s0 += GROUP) {
+    float ms[GROUP], ls[GROUP];
+    float4 a[GROUP], c[GROUP];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < GROUP; ++j) {
       const int s = s0 + j;
       const bool in = s < splits;
       ms[j] = in ? ml[2 * (int64_t)s * H] : -INFINITY;
@@ -1530,13 +1532,13 @@ __global__ __launch_bounds__(64 * kMergeSmallRows) void attn_merge_small_kernel(
     }
     float mg = M;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) mg = fmaxf(mg, ms[j]);
+    for (int j = 0; j < GROUP; ++j) mg = fmaxf(mg, ms[j]);
     const float f = __builtin_amdgcn_exp2f(M - mg);   // 0 on the first group
     L *= f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] *= f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < GROUP; ++j) {
       const float w = __builtin_amdgcn_exp2f(ms[j] - mg);   // 0 for the padding j
       L += w * ls[j];
       acc[0] += w * a[j].x; acc[1] += w * a[j].y; acc[2] += w * a[j].z; acc[3] += w * a[j].w;
@@ -1558,8 +1560,12 @@ hipError_t launch_merge(const float* part_o, const float* part_ml, int splits, i
                         uint16_t* out, float* lse, hipStream_t stream) {
   const int rows = T * H;
   if (splits <= kMergeSmallMax) {
-    hipLaunchKernelGGL(attn_merge_small_kernel, dim3((rows + kMergeSmallRows - 1) / kMergeSmallRows),
-                       dim3(64 * kMergeSmallRows), 0, stream, part_o, part_ml, splits, H, rows, out, lse);
+    if (splits > 8)
+      hipLaunchKernelGGL(attn_merge_small_kernel<16>, dim3((rows + kMergeSmallRows - 1) / kMergeSmallRows),
+                         dim3(64 * kMergeSmallRows), 0, stream, part_o, part_ml, splits, H, rows, out, lse);
+    else
+      hipLaunchKernelGGL(attn_merge_small_kernel<8>, dim3((rows + kMergeSmallRows - 1) / kMergeSmallRows),
+                         dim3(64 * kMergeSmallRows), 0, stream, part_o, part_ml, splits, H, rows, out, lse);
   } else {
     hipLaunchKernelGGL(attn_merge_kernel, dim3(rows), dim3(64 * kMergeWaves), 0, stream, part_o, part_ml,
                        splits, H, out, lse);
