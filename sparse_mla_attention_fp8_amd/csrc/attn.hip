@@ -54,7 +54,8 @@
 // row that finishes last merges them in the same launch: partials go through
 // device-coherent stores and loads, and an arrival word per (row, head group)
 // in the workspace names the last split.  Otherwise a merge kernel combines
-// them (attn_merge_small_kernel up to 16 splits, attn_merge_kernel beyond).
+// them (attn_merge_small_kernel up to 16 splits, attn_merge_kernel beyond,
+// attn_merge_spread_kernel beyond for calls of at most 64 (row, head) pairs).
 // m is kept in log2 units throughout.
 #include "common.h"
 
@@ -1417,6 +1418,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
 // L = 0 means the row has no valid entry.
 constexpr int kMergeWaves = 8;
 constexpr int kMergeUnroll = 8;
+constexpr int kMergeSpreadMaxRows = 64;   // up to this many (row, head) pairs: attn_merge_spread_kernel
 
 __global__ __launch_bounds__(64 * kMergeWaves) void attn_merge_kernel(const float* __restrict__ part_o,
                                                                       const float* __restrict__ part_ml,
@@ -1490,6 +1492,77 @@ __global__ __launch_bounds__(64 * kMergeWaves) void attn_merge_kernel(const floa
     pk[i] = bf16x2_rne(o[2 * i] * inv, o[2 * i + 1] * inv);
   *reinterpret_cast<uint4*>(out + (int64_t)th * kLatent + 8 * lane) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
   if (lse != nullptr && lane == 0) lse[th] = (Lt > 0.0f) ? (M + __log2f(Lt)) * kLn2 : -INFINITY;
+}
+
+
+// The same combination for calls with few (row, head) pairs and many splits
+// (a single decode row has up to 68): the 512 dims of a pair are spread over
+// four blocks of 128 (grid.y), so four times as many CUs pull the partials;
+// lane l of a wavefront owns dims 128 y + 2l and + 1.  Arithmetic and split
+// order as attn_merge_kernel.
+__global__ __launch_bounds__(64 * kMergeWaves) void attn_merge_spread_kernel(const float* __restrict__ part_o,
+                                                                             const float* __restrict__ part_ml,
+                                                                             int splits, int H,
+                                                                             uint16_t* __restrict__ out,
+                                                                             float* __restrict__ lse) {
+  __shared__ float2 po[kMergeWaves][64];
+  __shared__ float2 pml[kMergeWaves];
+  const int th = blockIdx.x;  // t * H + h
+  const int t = th / H, hh = th % H;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int d0 = blockIdx.y * 128 + 2 * lane;
+  const float* ml = part_ml + 2 * ((int64_t)t * splits * H + hh);   // split s at ml[2 * s * H]
+  const float* po_base = part_o + ((int64_t)t * splits * H + hh) * kLatent + d0;  // + s * H * 512
+  float acc0 = 0.0f, acc1 = 0.0f;
+  float Mw = -INFINITY, L = 0.0f;
+  for (int s0 = wave; s0 < splits; s0 += kMergeWaves * kMergeUnroll) {
+    float ms[kMergeUnroll], ls[kMergeUnroll];
+    float2 a[kMergeUnroll];
+#pragma unroll
+    for (int j = 0; j < kMergeUnroll; ++j) {
+      const int s = s0 + kMergeWaves * j;
+      const bool in = s < splits;
+      ms[j] = in ? ml[2 * (int64_t)s * H] : -INFINITY;
+      ls[j] = in ? ml[2 * (int64_t)s * H + 1] : 0.0f;
+      a[j] = in ? *reinterpret_cast<const float2*>(po_base + (int64_t)s * H * kLatent) : make_float2(0.0f, 0.0f);
+    }
+    float mg = Mw;
+#pragma unroll
+    for (int j = 0; j < kMergeUnroll; ++j) mg = fmaxf(mg, ms[j]);
+    const float f = __builtin_amdgcn_exp2f(Mw - mg);   // 0 on the first group
+    L *= f;
+    acc0 *= f;
+    acc1 *= f;
+#pragma unroll
+    for (int j = 0; j < kMergeUnroll; ++j) {
+      const float w = __builtin_amdgcn_exp2f(ms[j] - mg);   // 0 for the padding j
+      L += w * ls[j];
+      acc0 += w * a[j].x;
+      acc1 += w * a[j].y;
+    }
+    Mw = mg;
+  }
+  po[wave][lane] = make_float2(acc0, acc1);
+  if (lane == 0) pml[wave] = make_float2(Mw, L);
+  __syncthreads();
+  if (wave != 0) return;
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kMergeWaves; ++w) M = fmaxf(M, pml[w].x);
+  float o0 = 0.0f, o1 = 0.0f, Lt = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kMergeWaves; ++w) {
+    const float2 mlw = pml[w];
+    const float f = mlw.x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mlw.x - M);   // idle wavefronts
+    const float2 x = po[w][lane];
+    o0 += f * x.x;
+    o1 += f * x.y;
+    Lt += f * mlw.y;
+  }
+  const float inv = (Lt > 0.0f) ? 1.0f / Lt : 0.0f;
+  *reinterpret_cast<uint32_t*>(out + (int64_t)th * kLatent + d0) = bf16x2_rne(o0 * inv, o1 * inv);
+  if (lse != nullptr && lane == 0 && blockIdx.y == 0) lse[th] = (Lt > 0.0f) ? (M + __log2f(Lt)) * kLn2 : -INFINITY;
 }
 
 
@@ -1567,8 +1640,12 @@ hipError_t launch_merge(const float* part_o, const float* part_ml, int splits, i
       hipLaunchKernelGGL(attn_merge_small_kernel<8>, dim3((rows + kMergeSmallRows - 1) / kMergeSmallRows),
                          dim3(64 * kMergeSmallRows), 0, stream, part_o, part_ml, splits, H, rows, out, lse);
   } else {
-    hipLaunchKernelGGL(attn_merge_kernel, dim3(rows), dim3(64 * kMergeWaves), 0, stream, part_o, part_ml,
-                       splits, H, out, lse);
+    if (rows <= kMergeSpreadMaxRows)
+      hipLaunchKernelGGL(attn_merge_spread_kernel, dim3(rows, kLatent / 128), dim3(64 * kMergeWaves), 0, stream,
+                         part_o, part_ml, splits, H, out, lse);
+    else
+      hipLaunchKernelGGL(attn_merge_kernel, dim3(rows), dim3(64 * kMergeWaves), 0, stream, part_o, part_ml,
+                         splits, H, out, lse);
   }
   return hipGetLastError();
 }
