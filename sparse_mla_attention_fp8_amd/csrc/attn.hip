@@ -434,6 +434,14 @@ __device__ __noinline__ bool arrive_last(unsigned long long* word, unsigned long
   return count == splits;
 }
 
+// Wavefront priority for instruction issue on a SIMD (s_setprio): the index
+// scan, the gather issue and the partial-score reads ahead of it run at
+// kPrioIssue, the next chunk's operand reads and slot lookups at
+// kPrioOperands, the arithmetic at kPrioCompute.  With two workgroups per CU
+// the other workgroup's arithmetic then no longer delays a wavefront's
+// loads (1,024-row prefill 58.2 -> 55.8 us; decode shapes unchanged).
+constexpr int kPrioIssue = 2, kPrioOperands = 1, kPrioCompute = 0;
+
 // SMALL: the cache spans less than 4 GiB, so row byte offsets fit 32 bits.
 // WAVES: 8 (one workgroup per CU) or 4 (two per CU), see Geo.
 template <int ROPE, bool SMALL, int WAVES>
@@ -510,9 +518,11 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void attn_mfma_kern
   const int hi_k = range == 0 ? W : min(W, lo_k + range);
   // (its barriers also publish the staged q: each wavefront's first wait for
   // its index loads covers its earlier q loads)
+  __builtin_amdgcn_s_setprio(kPrioIssue);
   const int n = __builtin_amdgcn_readfirstlane(
       compact_valid<G::THREADS, kKeys>(idx + (int64_t)t * idx_stride, lo_k, hi_k, num_slots, slot_list,
                                        wave_counts, split, range == 0 ? splits : 0));
+  __builtin_amdgcn_s_setprio(kPrioCompute);
   const int nch = (n + kKeys - 1) / kKeys;
 
   // q, split below once the first gathers are in flight: latent score = qs *
@@ -707,7 +717,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void attn_mfma_kern
   const uint32_t lds0 = lds_addr(stages);
   if (nch > 0) {
     fetch_slots(0);
+    __builtin_amdgcn_s_setprio(kPrioIssue);
     issue(lds0, 0);
+    __builtin_amdgcn_s_setprio(kPrioCompute);
   }
 
   // q fragments of head n16: tile 2qh+u, dims 128(2qh+u) + 32g + 8k + [0, 8) -> qraw[4u + k]
@@ -777,7 +789,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void attn_mfma_kern
   for (int c = 1; c < kFirst; ++c)
     if (c < nch) {
       fetch_slots(c);
+      __builtin_amdgcn_s_setprio(kPrioIssue);
       issue(lds0 + (uint32_t)(c * G::STAGE), c);
+      __builtin_amdgcn_s_setprio(kPrioCompute);
     }
 
   // chunk 0: wait for it (the chunks issued after it stay in flight), score
@@ -790,7 +804,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void attn_mfma_kern
     // every wavefront has split q by now, so its stage can take its chunk
     if (G::NST - 1 < nch) {
       fetch_slots(G::NST - 1);
+      __builtin_amdgcn_s_setprio(kPrioIssue);
       issue(lds0 + (uint32_t)((G::NST - 1) * G::STAGE), G::NST - 1);
+      __builtin_amdgcn_s_setprio(kPrioCompute);
     }
     if (G::NST < nch) fetch_slots(G::NST);
     qk_finish(qk_mfma(qk_load(lds0)), 0);
@@ -810,6 +826,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void attn_mfma_kern
     // Chunk c's partial scores are read first, ahead of the gather issue:
     // LDS reads return in order, so the softmax then waits only for these, and
     // the issue runs while they are in flight.
+    __builtin_amdgcn_s_setprio(kPrioIssue);
     float4 u[2][2];
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb)
@@ -817,14 +834,17 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void attn_mfma_kern
       for (int h = 0; h < 2; ++h) u[bb][h] = xs[c & 1][2 * ps + bb][h][lane];
     const int cur = c % G::NST;
     if (c + G::NST < nch) issue(lds0 + (uint32_t)(cur * G::STAGE), c + G::NST);
+    __builtin_amdgcn_s_setprio(kPrioCompute);
 
     // ---- next chunk's operands (for the last chunk: stale bytes, results unused) ----
     // (the stage address as an opaque scalar, so that the compiler keeps one
     // base per read instead of one induction variable per address)
     const uint32_t nstg = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(((c + 1) % G::NST) * G::STAGE));
+    __builtin_amdgcn_s_setprio(kPrioOperands);
     const QkLoad nk = qk_load(nstg);
     read_pv(nstg, vn, scn);
     if (c + G::NST + 1 < nch) fetch_slots(c + G::NST + 1);
+    __builtin_amdgcn_s_setprio(kPrioCompute);
 
     // ---------------- softmax over keys 32ps + [0,32) of chunk c ----------------
     // An empty key half (last chunk) scores -inf throughout and adds exact zeros.
