@@ -117,7 +117,7 @@ def measured_traffic():
 def main():
     a = _args()
     if a.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (got --gpus {a.gpus}); the "
+        print(f"bench.py: the benchmark runs on one GPU only (got --gpus {a.gpus}); the "
               "multi-GPU sharding of the path is a design note, not a launchable mode.",
               file=sys.stderr)
         sys.exit(2)

@@ -74,7 +74,7 @@ extern "C" {
 #define SMLA_EINVAL       -1  /* bad argument (null pointer, size, alignment, rope_dim) */
 #define SMLA_EWORKSPACE   -2  /* workspace smaller than sparse_mla_attn_workspace_size() */
 #define SMLA_ELAUNCH      -3  /* the HIP runtime reported an error at launch */
-#define SMLA_EUNSUPPORTED -4  /* a size this build does not handle */
+#define SMLA_EUNSUPPORTED -4  /* a size the library does not handle */
 
 #define SMLA_ROW_BYTES   656
 #define SMLA_LATENT      512
